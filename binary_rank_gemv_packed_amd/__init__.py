@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libnq.so")
 NQ_OK, NQ_ERR_INVALID_ARG, NQ_ERR_NOT_PM1, NQ_ERR_WORKSPACE, NQ_ERR_UNSUPPORTED, NQ_ERR_HIP, NQ_ERR_INTERNAL = \
     0, -1, -2, -3, -4, -5, -6
 NQ_F32, NQ_F16, NQ_BF16 = 0, 1, 2
-PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "valu": 3}
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "valu": 3, "decode": 4}
 
 _DT = {torch.float32: NQ_F32, torch.float16: NQ_F16, torch.bfloat16: NQ_BF16}
 
@@ -54,8 +54,11 @@ def lib() -> ctypes.CDLL:
         "nq_pack_factors": (c_int, [P, vp, vp, vp, vp, vp, vp]),
         "nq_unpack_factors": (c_int, [P, vp, vp, vp]),
         "nq_workspace_bytes": (c_size, [P, c_int]),
+        "nq_workspace_bytes_path": (c_size, [P, c_int, c_int]),
         "nq_linear_fwd": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
         "nq_linear_fwd_path": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int]),
+        "nq_linear_fwd_profiled": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int, vp, c_int,
+                                           ctypes.POINTER(c_int)]),
         "nq_bits_per_weight": (ctypes.c_double, [c_int, c_int, c_int, c_int]),
         "nq_rank_for_bits": (c_int, [c_int, c_int, ctypes.c_double, c_int]),
         "nq_status_string": (ctypes.c_char_p, [c_int]),
@@ -135,8 +138,8 @@ def unpack(layer: Layer, stream=None):
     return U, V
 
 
-def workspace_bytes(layer: Layer, B: int) -> int:
-    return int(lib().nq_workspace_bytes(layer.ref, B))
+def workspace_bytes(layer: Layer, B: int, path: str = "auto") -> int:
+    return int(lib().nq_workspace_bytes_path(layer.ref, B, PATHS[path]))
 
 
 def new_workspace(layer: Layer, B: int) -> torch.Tensor:
@@ -157,6 +160,19 @@ def linear_into(x: torch.Tensor, layer: Layer, y: torch.Tensor, workspace: torch
     _check(lib().nq_linear_fwd_path(layer.ref, x.data_ptr(), _DT[x.dtype], y.data_ptr(), _DT[y.dtype], B,
                                     workspace.data_ptr(), workspace.numel(), _stream(stream), PATHS[path]))
     return y
+
+
+def linear_into_profiled(x: torch.Tensor, layer: Layer, y: torch.Tensor, workspace: torch.Tensor, events,
+                         path: str = "auto", stream=None) -> int:
+    """linear_into that records the given HIP events (raw hipEvent_t handles, as
+    ints) around each kernel launch; returns the number of launches."""
+    B = x.shape[0] if x.dim() == 2 else 1
+    arr = (ctypes.c_void_p * len(events))(*events)
+    nl = ctypes.c_int32(0)
+    _check(lib().nq_linear_fwd_profiled(layer.ref, x.data_ptr(), _DT[x.dtype], y.data_ptr(), _DT[y.dtype], B,
+                                        workspace.data_ptr(), workspace.numel(), _stream(stream), PATHS[path],
+                                        ctypes.cast(arr, ctypes.c_void_p), len(events), ctypes.byref(nl)))
+    return nl.value
 
 
 def linear(x: torch.Tensor, layer: Layer, out_dtype: torch.dtype | None = None, path: str = "auto",

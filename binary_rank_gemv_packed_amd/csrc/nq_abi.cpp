@@ -63,6 +63,10 @@ size_t plan_bytes(const nq_layer* L, int32_t B, int32_t path) {
     case NQ_PATH_GEMV: return nq::gemv_plan(L->m, L->n, L->r, B).bytes;
     case NQ_PATH_VALU: return nq::valu_plan(L->m, L->n, L->r).bytes;
     case NQ_PATH_GEMM: return nq::gemm_plan(L->m, L->n, L->r, B).bytes;
+    case NQ_PATH_DECODE: {
+      nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B);
+      return p.ok ? p.bytes : 0;
+    }
   }
   return 0;
 }
@@ -144,6 +148,10 @@ nq_status nq_unpack_factors(const nq_layer* L, int8_t* U, int8_t* V, nq_stream_t
 size_t nq_workspace_bytes(const nq_layer* L, int32_t B) {
   if (check_layer(L) || B <= 0 || B > MAX_BATCH) return 0;
   size_t need = plan_bytes(L, B, NQ_PATH_GEMM);
+  if (B <= 4) {
+    size_t d = plan_bytes(L, B, NQ_PATH_DECODE);
+    need = d > need ? d : need;
+  }
   if (B <= 16) {
     size_t g = plan_bytes(L, B, NQ_PATH_GEMV);
     need = g > need ? g : need;
@@ -155,12 +163,23 @@ size_t nq_workspace_bytes(const nq_layer* L, int32_t B) {
   return need;
 }
 
-nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
-                             void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path) {
+size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path) {
+  if (check_layer(L) || B <= 0 || B > MAX_BATCH) return 0;
+  if (path == NQ_PATH_AUTO) return nq_workspace_bytes(L, B);
+  if (path == NQ_PATH_GEMV && B > 16) return 0;
+  if (path == NQ_PATH_VALU && B != 1) return 0;
+  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B).ok) return 0;
+  if (path < NQ_PATH_AUTO || path > NQ_PATH_DECODE) return 0;
+  return plan_bytes(L, B, path);
+}
+
+static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
+                          void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path,
+                          nq::LaunchMarks* marks) {
   nq_status st = check_layer(L);
   if (st) return st;
   if (B < 0 || B > MAX_BATCH) return fail(NQ_ERR_INVALID_ARG, "batch %d out of range 0..%d", B, MAX_BATCH);
-  if (path < NQ_PATH_AUTO || path > NQ_PATH_VALU) return fail(NQ_ERR_INVALID_ARG, "unknown path %d", path);
+  if (path < NQ_PATH_AUTO || path > NQ_PATH_DECODE) return fail(NQ_ERR_INVALID_ARG, "unknown path %d", path);
   const int xb = act_bytes(x_dtype), yb = act_bytes(y_dtype);
   if (!xb) return fail(NQ_ERR_INVALID_ARG, "x_dtype %d is not NQ_BF16 or NQ_F32", x_dtype);
   if (!yb) return fail(NQ_ERR_INVALID_ARG, "y_dtype %d is not NQ_BF16 or NQ_F32", y_dtype);
@@ -173,9 +192,16 @@ nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, 
     uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + (uintptr_t)B * L->m * yb;
     if (x0 < y1 && y0 < x1) return fail(NQ_ERR_INVALID_ARG, "x and y overlap");
   }
-  if (path == NQ_PATH_AUTO) path = B <= 16 ? NQ_PATH_GEMV : NQ_PATH_GEMM;
+  if (path == NQ_PATH_AUTO) {
+    if (B <= 4 && nq::dec_plan(L->m, L->n, L->r, B).ok) path = NQ_PATH_DECODE;
+    else path = B <= 16 ? NQ_PATH_GEMV : NQ_PATH_GEMM;
+  }
   if (path == NQ_PATH_GEMV && B > 16) return fail(NQ_ERR_UNSUPPORTED, "gemv path takes B <= 16 (got %d)", B);
   if (path == NQ_PATH_VALU && B != 1) return fail(NQ_ERR_UNSUPPORTED, "valu path takes B == 1 (got %d)", B);
+  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B).ok)
+    return fail(NQ_ERR_UNSUPPORTED, "decode path takes B <= 4 and a rank whose image fits in LDS (B=%d r=%d)", B,
+                L->r);
+  if (path == NQ_PATH_GEMM) return fail(NQ_ERR_UNSUPPORTED, "the B > 16 path is not available (B=%d)", B);
   const size_t need = plan_bytes(L, B, path);
   if (workspace_bytes < need)
     return fail(NQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
@@ -196,15 +222,36 @@ nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, 
   a.ws = static_cast<uint8_t*>(workspace);
   a.ws_bytes = workspace_bytes;
   a.stream = reinterpret_cast<hipStream_t>(stream);
+  a.marks = marks;
+  if (marks && path != NQ_PATH_DECODE)
+    return fail(NQ_ERR_UNSUPPORTED, "timing marks are recorded by the decode path only");
   (void)hipGetLastError();
   hipError_t e;
   switch (path) {
     case NQ_PATH_GEMV: e = nq::gemv_forward(a, nq::gemv_plan(a.m, a.n, a.r, B)); break;
     case NQ_PATH_VALU: e = nq::valu_forward(a, nq::valu_plan(a.m, a.n, a.r)); break;
+    case NQ_PATH_DECODE: e = nq::dec_forward(a, nq::dec_plan(a.m, a.n, a.r, B)); break;
     default: e = nq::gemm_forward(a, nq::gemm_plan(a.m, a.n, a.r, B)); break;
   }
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return ok();
+}
+
+nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
+                             void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path) {
+  return fwd_impl(L, x, x_dtype, y, y_dtype, B, workspace, workspace_bytes, stream, path, nullptr);
+}
+
+nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
+                                 int32_t B, void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path,
+                                 void* const* events, int32_t n_events, int32_t* n_launches) {
+  if (!events || n_events < 1 || !n_launches) return fail(NQ_ERR_INVALID_ARG, "events and n_launches must be given");
+  nq::LaunchMarks marks;
+  marks.ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  marks.n = n_events;
+  nq_status st = fwd_impl(L, x, x_dtype, y, y_dtype, B, workspace, workspace_bytes, stream, path, &marks);
+  *n_launches = marks.k > 0 ? marks.k - 1 : 0;
+  return st;
 }
 
 nq_status nq_linear_fwd(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,

@@ -89,7 +89,9 @@ __device__ void build_tile_image(float v, int kt, int b, const ImgOut& o, float*
   const int k = threadIdx.x;
   const int G = b / o.TPG, tb = b % o.TPG;
   const float c = plane_factor(k);
-  float res = v / c;
+  // a non-finite value gets no pieces; it reaches the output through the sum term
+  const bool fin = __builtin_isfinite(v);
+  float res = fin ? v / c : 0.0f;
   float recon = 0.0f;
   const size_t tbase = (size_t)(kt * o.NG + G) * 64;
   for (int q = 0; q < o.P; q++) {
@@ -109,7 +111,7 @@ __device__ void build_tile_image(float v, int kt, int b, const ImgOut& o, float*
     o.xq[(tbase + lane) * IMG_LANE_BYTES + byte] = (uint8_t)encode_e4m3(p);
     if ((k & 31) == 0) o.xs[tbase + col + 16 * (k >> 5)] = (uint32_t)(e + 127);
   }
-  float s = block128_sum(recon * c, red);
+  float s = block128_sum(fin ? recon * c : v, red);
   if (k == 0) o.xsum[(size_t)b * o.KT + kt] = s;
 }
 

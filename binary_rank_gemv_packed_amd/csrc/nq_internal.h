@@ -13,6 +13,18 @@ hipError_t launch_unpack(const uint32_t* in, int R, int C, long long ld_row, lon
                          hipStream_t s);
 
 // dtype codes match nq_dtype: 0 = f32, 1 = f16, 2 = bf16.
+// Optional timing marks: event k is recorded on the stream just before the
+// k-th kernel launch of a forward, and one more after the last launch.
+struct LaunchMarks {
+  hipEvent_t* ev = nullptr;
+  int n = 0;
+  int k = 0;
+  void mark(hipStream_t s) {
+    if (ev && k < n) hipEventRecord(ev[k], s);
+    k++;
+  }
+};
+
 struct FwdArgs {
   int m, n, r, B;
   int scale_dtype, x_dtype, y_dtype;
@@ -22,7 +34,12 @@ struct FwdArgs {
   uint8_t* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  LaunchMarks* marks = nullptr;  // null: no timing marks
 };
+
+inline void mark(const FwdArgs& a) {
+  if (a.marks) a.marks->mark(a.stream);
+}
 
 // Work split of one sign-matrix product over wavefronts: each wave handles one
 // 16-row tile and kt_per_split column tiles (a multiple of 4).
@@ -45,6 +62,22 @@ struct GemvPlan {
 };
 GemvPlan gemv_plan(int m, int n, int r, int B);
 hipError_t gemv_forward(const FwdArgs& a, const GemvPlan& p);
+
+// Batch 1..4 decode path (nq_dec.hip).  Stage 1 runs on S1 column splits of
+// KL1 tiles with RG1 row tiles per workgroup; stage 2 on RG2 row tiles x KS2
+// column parts per workgroup.  fused_mid: stage 2 builds the image of t' itself.
+struct DecPlan {
+  bool ok, fused_mid;
+  int B, CW;
+  int RT1, KT1, RG1, KL1, S1, KS1, Rpad1;
+  int RT2, KT2, RG2, KS2;
+  int QM1, QM2;  // most quads one wave of stage 1 / stage 2 streams per row tile
+  size_t lds1, lds2, red1, red2;
+  size_t off_img1, off_part, off_img2;
+  size_t bytes;
+};
+DecPlan dec_plan(int m, int n, int r, int B);
+hipError_t dec_forward(const FwdArgs& a, const DecPlan& p);
 
 struct ValuPlan {
   StagePlan s1, s2;

@@ -52,9 +52,12 @@ typedef enum { NQ_F32 = 0, NQ_F16 = 1, NQ_BF16 = 2 } nq_dtype;
 /* Which kernels run the forward.  AUTO picks by batch size. */
 typedef enum {
   NQ_PATH_AUTO = 0,
-  NQ_PATH_GEMV = 1, /* 1 <= B <= 16: sign bits as fp4 MFMA operands, activations as fp8 pieces */
-  NQ_PATH_GEMM = 2, /* any B: sign bits expanded to fp16 +-1 in registers, fp16 MFMA          */
-  NQ_PATH_VALU = 3  /* B == 1 only: plain per-bit masked sums on the vector ALU (comparison)  */
+  NQ_PATH_GEMV = 1,   /* 1 <= B <= 16: sign bits as fp4 MFMA operands, activations as fp8
+                         pieces read from global images (4 or 5 launches)                    */
+  NQ_PATH_GEMM = 2,   /* B > 16 (prefill); NQ_ERR_UNSUPPORTED until its kernels exist       */
+  NQ_PATH_VALU = 3,   /* B == 1 only: plain per-bit masked sums on the vector ALU (comparison) */
+  NQ_PATH_DECODE = 4  /* 1 <= B <= 4: the decode path, activation images staged in LDS
+                         (3 launches, 4 when the stage-1 partials are too many to fold)      */
 } nq_path;
 
 /* A packed layer.  `blob` is device memory of nq_layer_bytes(m, n, r, scale_dtype)
@@ -100,6 +103,10 @@ nq_status nq_unpack_factors(const nq_layer* L, int8_t* U, int8_t* V, nq_stream_t
  * for other use between calls. */
 size_t nq_workspace_bytes(const nq_layer* L, int32_t B);
 
+/* Bytes of workspace one path needs for batch B (nq_path); 0 when the path does
+ * not take B or for invalid arguments.  NQ_PATH_AUTO gives nq_workspace_bytes. */
+size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path);
+
 /* y = x W_hat^T for a batch of B rows.
  *   x : device, B x n row-major, x_dtype NQ_BF16 or NQ_F32, 4-byte aligned
  *   y : device, B x m row-major, y_dtype NQ_BF16 or NQ_F32, 4-byte aligned; must not overlap x
@@ -117,6 +124,18 @@ nq_status nq_linear_fwd(const nq_layer* L, const void* x, int32_t x_dtype, void*
 nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, void* y,
                              int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
                              nq_stream_t stream, int32_t path);
+
+/* As nq_linear_fwd_path, and for timing each kernel of the call: records
+ * events[k] (hipEvent_t handles created by the caller) on `stream` just before
+ * the k-th kernel launch and events[K] after the last of the K launches, for
+ * the first n_events of them; *n_launches receives K.  Only NQ_PATH_DECODE
+ * (or AUTO resolving to it) records marks; other paths return
+ * NQ_ERR_UNSUPPORTED.  The launches are those of nq_linear_fwd_path, in order
+ * (decode: activation image, stage 1, [mid image,] stage 2). */
+nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dtype, void* y,
+                                 int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
+                                 nq_stream_t stream, int32_t path, void* const* events,
+                                 int32_t n_events, int32_t* n_launches);
 
 /* Average bits per original weight: (r(m+n) + scale_bits (m+n+r)) / (m n)
  * (hardwired.dev, sections "Jak NanoQuant funguje" and 'Co znamena

@@ -52,3 +52,32 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (nearest, ties to even) via fp32."""
     import synth
     return synth.round_to_bf16(np.asarray(a, np.float32).astype(np.float32)).astype(np.float64)
+
+
+def bf16_ulp(a: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at the magnitude of each value (8 significand bits)."""
+    a = np.abs(np.asarray(a, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_bf16_output(ybf, ref, y32=None, tol=TOL):
+    """bf16 output against the fp64 oracle.
+
+    * With the same call's fp32 output y32 (the kernels round their fp32 result
+      once, to nearest even): ybf must be exactly bf16(y32), bit for bit.
+    * Per element: |ybf - bf16(ref)| <= 1 bf16 ulp + 2 |y32 - ref|.  A plain
+      one-ulp bar is wrong for outputs near zero, where the fp32 sum's absolute
+      error (bounded in relative L2 by the fp32 check) exceeds that element's
+      bf16 ulp; the fp32 error term covers exactly that.
+    * Whole output: relative L2 within the tolerance plus the error that
+      rounding the exact result to bf16 costs by itself."""
+    ybf = np.asarray(ybf, np.float64)
+    rref = bf16_round(ref)
+    if y32 is not None:
+        y32 = np.asarray(y32, np.float64)
+        assert np.array_equal(ybf, bf16_round(y32))
+        slack = bf16_ulp(rref) * (1 + 1e-9) + 2.0 * np.abs(y32 - ref)
+        diff = np.abs(ybf - rref)
+        assert np.all(diff <= slack), float(np.max(diff / slack))
+    assert rel_l2(ybf, ref) <= tol + rel_l2(rref, ref)

@@ -113,6 +113,9 @@ def test_fwd_validation_errors(L):
     assert fwd(L, _layer(), ws=FAKE + (2 << 30) + 128) == E.NQ_ERR_INVALID_ARG
     assert fwd(L, _layer(), B=17, path=nq.PATHS["gemv"]) == E.NQ_ERR_UNSUPPORTED
     assert fwd(L, _layer(), B=2, path=nq.PATHS["valu"]) == E.NQ_ERR_UNSUPPORTED
+    assert fwd(L, _layer(), B=5, path=nq.PATHS["decode"]) == E.NQ_ERR_UNSUPPORTED
+    assert fwd(L, _layer(), B=17) == E.NQ_ERR_UNSUPPORTED        # no B > 16 path yet
+    assert fwd(L, _layer(), B=17, path=nq.PATHS["gemm"]) == E.NQ_ERR_UNSUPPORTED
     assert b"overlap" not in L.nq_last_error()
     fwd(L, _layer(), y=FAKE + 64)
     assert b"overlap" in L.nq_last_error()
@@ -130,7 +133,14 @@ def test_workspace_bytes(L):
     assert L.nq_workspace_bytes(None, 1) == 0
     w1 = L.nq_workspace_bytes(ref, 1)
     assert 0 < w1 < 64 << 20
-    assert fwd(L, lay, wsb=w1 - 1) == nq.NQ_ERR_WORKSPACE
+    for name in ("decode", "gemv", "valu"):
+        need = L.nq_workspace_bytes_path(ref, 1, nq.PATHS[name])
+        assert 0 < need <= w1
+        assert fwd(L, lay, wsb=need - 1, path=nq.PATHS[name]) == nq.NQ_ERR_WORKSPACE
+    assert L.nq_workspace_bytes_path(ref, 5, nq.PATHS["decode"]) == 0
+    assert L.nq_workspace_bytes_path(ref, 17, nq.PATHS["gemv"]) == 0
+    assert L.nq_workspace_bytes_path(ref, 2, nq.PATHS["valu"]) == 0
+    assert L.nq_workspace_bytes_path(ref, 1, 99) == 0
 
 
 def test_pack_validation_errors(L):
