@@ -201,7 +201,6 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B).ok)
     return fail(NQ_ERR_UNSUPPORTED, "decode path takes B <= 4 and a rank whose image fits in LDS (B=%d r=%d)", B,
                 L->r);
-  if (path == NQ_PATH_GEMM) return fail(NQ_ERR_UNSUPPORTED, "the B > 16 path is not available (B=%d)", B);
   const size_t need = plan_bytes(L, B, path);
   if (workspace_bytes < need)
     return fail(NQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);

@@ -1,19 +1,292 @@
-// Large-batch forward ("gemm" path): placeholder until the fp16 MFMA kernels land.
+// Large-batch forward ("gemm" path, prefill): both sign-matrix products as
+// dense fp16 MFMA GEMMs with the sign bits unpacked to exact fp16 +-1 in LDS.
+//
+//   prep  : X' = s2 * x per row, scaled by a per-row power of two 2^-e and
+//           rounded to fp16 (columns padded to whole 128-column tiles with 0)
+//   gemm  : T = X' V             (fp32, rows rescaled by 2^e)
+//   mid   : T' = g * T per row, scaled by a per-row power of two, fp16
+//   gemm  : y = s1 * (T' U^T)    (rows rescaled, stored as fp32 or bf16)
+//
+// The sign operand is exact in fp16.  The activation operand is rounded to
+// fp16 (11 significant bits, relative error <= 2^-11 per value) after a
+// power-of-two row scale that puts the row maximum in [2^13, 2^14), so no value
+// overflows and the scale is undone exactly in the fp32 epilogue.  At B = 2048
+// the work is a dense contraction (2 B r (m + n) flops, ~2.8 TFLOP per 70B
+// block), so it runs on the matrix cores rather than as B separate GEMVs.
 #include "nq_common.h"
 #include "nq_internal.h"
 
 namespace nq {
 
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, BKG = 32;  // block tile and K step
+constexpr int LDA_S = BKG + 8;               // LDS row stride in halves (pad against bank conflicts)
+constexpr int TARGET_EXP = 13;               // row maximum lands in [2^13, 2^14)
+
+__device__ inline int frexp_exp(float a) { return __builtin_amdgcn_frexp_expf(a); }
+
+template <typename T> __device__ inline float ldf(const T* p, size_t i);
+template <> __device__ inline float ldf<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ inline float ldf<_Float16>(const _Float16* p, size_t i) { return (float)p[i]; }
+template <> __device__ inline float ldf<uint16_t>(const uint16_t* p, size_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+__device__ inline float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); i++) m = fmaxf(m, red[i]);
+  __syncthreads();
+  return m;
+}
+
+// Exponent e with max * 2^-e in [2^TARGET_EXP, 2^(TARGET_EXP+1)); 0 for a
+// zero or non-finite row (non-finite values then stay non-finite in fp16).
+__device__ inline int row_exp(float mx) {
+  if (!(mx > 0.0f) || !(mx <= 3.4028235e38f)) return 0;
+  return (frexp_exp(mx) - 1) - TARGET_EXP;
+}
+
+// One workgroup (256 threads) per row: out[row][k] = fp16(scale_in[k] * in[row][k] * 2^-e)
+// for k < K, 0 for K <= k < Kpad; rexp[row] = e.
+template <typename IT, typename ST>
+__global__ void __launch_bounds__(256) row_to_f16_kernel(const IT* __restrict__ in, size_t ld_in,
+                                                         const ST* __restrict__ scale, int K, int Kpad,
+                                                         _Float16* __restrict__ out, int* __restrict__ rexp) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const IT* src = in + (size_t)row * ld_in;
+  float mx = 0.0f;
+  for (int k = threadIdx.x; k < K; k += 256) mx = fmaxf(mx, fabsf(ldf(src, k) * ldf(scale, k)));
+  mx = block_max(mx, red);
+  const int e = row_exp(mx);
+  const float f = __builtin_ldexpf(1.0f, -e);
+  _Float16* dst = out + (size_t)row * Kpad;
+  for (int k = threadIdx.x; k < Kpad; k += 256) dst[k] = k < K ? (_Float16)(ldf(src, k) * ldf(scale, k) * f) : (_Float16)0.0f;
+  if (threadIdx.x == 0) rexp[row] = e;
+}
+
+// C = 2^e_row * (A W^T): A [M x Kpad] fp16 row-major (lda = Kpad), W the packed
+// sign matrix with N rows and KT column tiles (Kpad = 128 KT).  EPI 0: fp32 out
+// (ldc); EPI 1: out = colscale[n] * C as fp32 (ydt 0) or bf16 (ydt 2).
+struct GemmArgs {
+  const _Float16* A;
+  const int* rexp;
+  const uint32_t* W;
+  int M, N, KT;
+  void* C;
+  size_t ldc;
+  const void* colscale;
+  int ydt;
+  int MB, NB;  // block counts
+};
+
+// Unpacks one packed word (row n, columns 32g .. 32g+31 of a tile, bit 4p+j =
+// column 8j+p, bit 1 = +1) into 32 fp16 +-1 values in column order.
+__device__ __forceinline__ uint4 unpack_plane(uint32_t nw, int j) {
+  const uint32_t t = (nw >> j) & 0x11111111u;  // bit 4p = "column 8j+p is -1"
+  uint32_t d[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint32_t two = (t >> (8 * q)) & 0x11u;              // bits 0 and 4: columns 2q, 2q+1
+    d[q] = ((two * 0x08008000u) & 0x80008000u) | 0x3C003C00u;  // sign bits 15 and 31 on +-1.0
+  }
+  return uint4{d[0], d[1], d[2], d[3]};
+}
+
+__device__ __forceinline__ void unpack_word(uint32_t w, uint4& u0, uint4& u1, uint4& u2, uint4& u3) {
+  const uint32_t nw = ~w;
+  u0 = unpack_plane(nw, 0);
+  u1 = unpack_plane(nw, 1);
+  u2 = unpack_plane(nw, 2);
+  u3 = unpack_plane(nw, 3);
+}
+
+template <int EPI, typename SC>
+__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
+  __shared__ __align__(16) _Float16 As[2][BM * LDA_S];
+  __shared__ __align__(16) _Float16 Ws[2][BN * LDA_S];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware tile order: the 8 XCDs take contiguous runs of tiles, M-block
+  // major, so the workgroups one XCD runs together share an activation block
+  const int T = a.MB * a.NB;
+  const int per = (T + 7) / 8;
+  const int id = blockIdx.x;
+  const int t = (id % 8) * per + id / 8;
+  if (t >= T) return;
+  const int mb = t / a.NB, nb = t % a.NB;
+  const int m0 = mb * BM, n0 = nb * BN;
+  const int Kpad = a.KT * 128;
+  const int nk = Kpad / BKG;
+
+  // global -> register staging: A 128 rows x 32 halves (2 x 16 B per thread),
+  // W 8 row tiles x 16 words (threads 0..127, one word each)
+  const int a_row = tid >> 1, a_col = (tid & 1) * 16;
+  const int a_grow = min(m0 + a_row, a.M - 1);
+  const _Float16* a_src = a.A + (size_t)a_grow * Kpad + a_col;
+  const int w_rt = tid >> 4, w_l = tid & 15;               // row tile in block, row in tile
+  const int w_row = n0 + w_rt * 16 + w_l;
+  const bool w_active = tid < 128;
+  const int w_rtg = min((n0 >> 4) + w_rt, (a.N + 15) / 16 - 1);
+  const uint32_t* w_tile = a.W + (size_t)w_rtg * a.KT * 64;
+
+  uint4 ra0, ra1;
+  uint32_t rw = 0;
+#define NQ_GLOAD(ks)                                                          \
+  do {                                                                        \
+    const int k0_ = (ks) * BKG;                                               \
+    const uint4* s_ = reinterpret_cast<const uint4*>(a_src + k0_);            \
+    ra0 = s_[0];                                                              \
+    ra1 = s_[1];                                                              \
+    if (w_active) {                                                           \
+      const int kt_ = k0_ >> 7, g_ = (k0_ >> 5) & 3;                          \
+      const int q_ = kt_ >> 2;                                                \
+      const int f_ = min(4, a.KT - 4 * q_);                                   \
+      rw = w_tile[(size_t)q_ * 256 + (w_l + 16 * g_) * f_ + (kt_ & 3)];       \
+    }                                                                         \
+  } while (0)
+#define NQ_LSTORE(buf)                                                                    \
+  do {                                                                                    \
+    uint4* da_ = reinterpret_cast<uint4*>(&As[(buf)][a_row * LDA_S + a_col]);             \
+    da_[0] = ra0;                                                                         \
+    da_[1] = ra1;                                                                         \
+    if (w_active) {                                                                       \
+      uint4 u0_, u1_, u2_, u3_;                                                           \
+      unpack_word(rw, u0_, u1_, u2_, u3_);                                                \
+      uint4* dw_ = reinterpret_cast<uint4*>(&Ws[(buf)][(w_rt * 16 + w_l) * LDA_S]);       \
+      dw_[0] = u0_;                                                                       \
+      dw_[1] = u1_;                                                                       \
+      dw_[2] = u2_;                                                                       \
+      dw_[3] = u3_;                                                                       \
+    }                                                                                     \
+  } while (0)
+  (void)w_row;
+
+  // wave tile 64 x 64 = 4 x 4 MFMA tiles of 16 x 16
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  NQ_GLOAD(0);
+  NQ_LSTORE(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;  // fragment row/column and K offset
+  for (int ks = 0; ks < nk; ks++) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) NQ_GLOAD(ks + 1);
+    h8 af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) af[i] = *reinterpret_cast<const h8*>(&As[buf][(wm + 16 * i + fr) * LDA_S + fk]);
+#pragma unroll
+    for (int j = 0; j < 4; j++) bf[j] = *reinterpret_cast<const h8*>(&Ws[buf][(wn + 16 * j + fr) * LDA_S + fk]);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    if (ks + 1 < nk) NQ_LSTORE(buf ^ 1);
+    __syncthreads();
+  }
+
+#undef NQ_GLOAD
+#undef NQ_LSTORE
+  // epilogue: lane holds rows 4 * (lane >> 4) + v of each 16 x 16 tile, column lane & 15
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int row = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
+      if (row >= a.M) continue;
+      const float rs = __builtin_ldexpf(1.0f, a.rexp[row]);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int col = n0 + wn + 16 * j + (lane & 15);
+        if (col >= a.N) continue;
+        const float c = acc[i][j][v] * rs;
+        if (EPI == 0) {
+          reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] = c;
+        } else {
+          const float yv = c * ldf(reinterpret_cast<const SC*>(a.colscale), col);
+          const size_t yi = (size_t)row * a.ldc + col;
+          if (a.ydt == 0) reinterpret_cast<float*>(a.C)[yi] = yv;
+          else reinterpret_cast<uint16_t*>(a.C)[yi] = f32_to_bf16(yv);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
 GemmPlan gemm_plan(int m, int n, int r, int B) {
   GemmPlan p{};
-  (void)m; (void)n; (void)r; (void)B;
-  p.bytes = 0;
+  p.Bpad = B;
+  p.KT1 = ceil_div(n, 128);  // stage 1 contraction: inputs
+  p.KT2 = ceil_div(r, 128);  // stage 2 contraction: rank
+  p.RT1 = ceil_div(r, 16);
+  p.RT2 = ceil_div(m, 16);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  p.off_x16 = take((size_t)B * p.KT1 * 128 * 2);  // X' fp16
+  p.off_xexp = take((size_t)B * 4);
+  p.off_t32 = take((size_t)B * r * 4);            // T fp32
+  p.off_t16 = take((size_t)B * p.KT2 * 128 * 2);  // T' fp16
+  p.off_texp = take((size_t)B * 4);
+  p.bytes = o;
   return p;
 }
 
+template <typename XT, typename ST>
+static hipError_t gemm_forward_t(const FwdArgs& a, const GemmPlan& p) {
+  const BlobLayout L = blob_layout(a.m, a.n, a.r, sizeof(ST));
+  const uint32_t* U = reinterpret_cast<const uint32_t*>(a.blob + L.off_u);
+  const uint32_t* Vt = reinterpret_cast<const uint32_t*>(a.blob + L.off_vt);
+  const ST* s1 = reinterpret_cast<const ST*>(a.blob + L.off_s1);
+  const ST* g = reinterpret_cast<const ST*>(a.blob + L.off_g);
+  const ST* s2 = reinterpret_cast<const ST*>(a.blob + L.off_s2);
+  _Float16* x16 = reinterpret_cast<_Float16*>(a.ws + p.off_x16);
+  int* xexp = reinterpret_cast<int*>(a.ws + p.off_xexp);
+  float* t32 = reinterpret_cast<float*>(a.ws + p.off_t32);
+  _Float16* t16 = reinterpret_cast<_Float16*>(a.ws + p.off_t16);
+  int* texp = reinterpret_cast<int*>(a.ws + p.off_texp);
+  hipStream_t st = a.stream;
+  const int B = a.B;
+
+  mark(a);
+  hipLaunchKernelGGL((row_to_f16_kernel<XT, ST>), dim3(B), dim3(256), 0, st, reinterpret_cast<const XT*>(a.x),
+                     (size_t)a.n, s2, a.n, p.KT1 * 128, x16, xexp);
+  GemmArgs g1{x16, xexp, Vt, B, a.r, p.KT1, t32, (size_t)a.r, nullptr, 0, ceil_div(B, BM), ceil_div(a.r, BN)};
+  mark(a);
+  hipLaunchKernelGGL((gemm_kernel<0, ST>), dim3(8 * ceil_div(g1.MB * g1.NB, 8)), dim3(256), 0, st, g1);
+  mark(a);
+  hipLaunchKernelGGL((row_to_f16_kernel<float, ST>), dim3(B), dim3(256), 0, st, t32, (size_t)a.r, g, a.r,
+                     p.KT2 * 128, t16, texp);
+  GemmArgs g2{t16, texp, U, B, a.m, p.KT2, a.y, (size_t)a.m, s1, a.y_dtype == 0 ? 0 : 2, ceil_div(B, BM),
+              ceil_div(a.m, BN)};
+  mark(a);
+  hipLaunchKernelGGL((gemm_kernel<1, ST>), dim3(8 * ceil_div(g2.MB * g2.NB, 8)), dim3(256), 0, st, g2);
+  mark(a);
+  return hipGetLastError();
+}
+
 hipError_t gemm_forward(const FwdArgs& a, const GemmPlan& p) {
-  (void)a; (void)p;
-  return hipErrorNotSupported;
+  if (a.x_dtype == 2) {
+    return a.scale_dtype == 1 ? gemm_forward_t<uint16_t, _Float16>(a, p) : gemm_forward_t<uint16_t, float>(a, p);
+  }
+  return a.scale_dtype == 1 ? gemm_forward_t<float, _Float16>(a, p) : gemm_forward_t<float, float>(a, p);
 }
 
 }  // namespace nq

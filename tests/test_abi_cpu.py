@@ -114,8 +114,7 @@ def test_fwd_validation_errors(L):
     assert fwd(L, _layer(), B=17, path=nq.PATHS["gemv"]) == E.NQ_ERR_UNSUPPORTED
     assert fwd(L, _layer(), B=2, path=nq.PATHS["valu"]) == E.NQ_ERR_UNSUPPORTED
     assert fwd(L, _layer(), B=5, path=nq.PATHS["decode"]) == E.NQ_ERR_UNSUPPORTED
-    assert fwd(L, _layer(), B=17) == E.NQ_ERR_UNSUPPORTED        # no B > 16 path yet
-    assert fwd(L, _layer(), B=17, path=nq.PATHS["gemm"]) == E.NQ_ERR_UNSUPPORTED
+    assert fwd(L, _layer(), B=17, wsb=16) == E.NQ_ERR_WORKSPACE   # B > 16: the prefill path's workspace
     assert b"overlap" not in L.nq_last_error()
     fwd(L, _layer(), y=FAKE + 64)
     assert b"overlap" in L.nq_last_error()
@@ -141,6 +140,10 @@ def test_workspace_bytes(L):
     assert L.nq_workspace_bytes_path(ref, 17, nq.PATHS["gemv"]) == 0
     assert L.nq_workspace_bytes_path(ref, 2, nq.PATHS["valu"]) == 0
     assert L.nq_workspace_bytes_path(ref, 1, 99) == 0
+    # prefill: X' fp16 + T fp32 + T' fp16 for 2048 tokens
+    big = L.nq_workspace_bytes_path(ref, 2048, nq.PATHS["gemm"])
+    assert big >= 2048 * (64 * 128 * 2 + 5079 * 4 + 40 * 128 * 2)
+    assert L.nq_workspace_bytes(ref, 2048) == big
 
 
 def test_pack_validation_errors(L):
