@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         "nq_linear_fwd_path": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int]),
         "nq_linear_fwd_profiled": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int, vp, c_int,
                                            ctypes.POINTER(c_int)]),
+        "nq_linear_fwd_noalloc": (c_int, [P, vp, c_int, vp, c_int, c_int, vp]),
         "nq_bits_per_weight": (ctypes.c_double, [c_int, c_int, c_int, c_int]),
         "nq_rank_for_bits": (c_int, [c_int, c_int, ctypes.c_double, c_int]),
         "nq_status_string": (ctypes.c_char_p, [c_int]),
@@ -173,6 +174,21 @@ def linear_into_profiled(x: torch.Tensor, layer: Layer, y: torch.Tensor, workspa
                                         workspace.data_ptr(), workspace.numel(), _stream(stream), PATHS[path],
                                         ctypes.cast(arr, ctypes.c_void_p), len(events), ctypes.byref(nl)))
     return nl.value
+
+
+def linear_noalloc_into(x: torch.Tensor, layer: Layer, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """linear_into without a workspace: the library's static device scratch is
+    used (see nq_linear_fwd_noalloc; calls overlapping on one GPU race)."""
+    B = x.shape[0] if x.dim() == 2 else 1
+    if x.dtype not in (torch.bfloat16, torch.float32) or y.dtype not in (torch.bfloat16, torch.float32):
+        raise NQError(NQ_ERR_INVALID_ARG, "x and y must be bf16 or fp32")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise NQError(NQ_ERR_INVALID_ARG, "x and y must be contiguous")
+    if x.numel() != B * layer.n or y.numel() != B * layer.m:
+        raise NQError(NQ_ERR_INVALID_ARG, "x or y has the wrong number of elements")
+    _check(lib().nq_linear_fwd_noalloc(layer.ref, x.data_ptr(), _DT[x.dtype], y.data_ptr(), _DT[y.dtype], B,
+                                       _stream(stream)))
+    return y
 
 
 def linear(x: torch.Tensor, layer: Layer, out_dtype: torch.dtype | None = None, path: str = "auto",

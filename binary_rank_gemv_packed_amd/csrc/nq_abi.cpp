@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "nq_common.h"
@@ -173,6 +174,19 @@ size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path) {
   return plan_bytes(L, B, path);
 }
 
+static int32_t auto_path(const nq_layer* L, int32_t B) {
+  if (B <= 4 && nq::dec_plan(L->m, L->n, L->r, B).ok) return NQ_PATH_DECODE;
+  return B <= 16 ? NQ_PATH_GEMV : NQ_PATH_GEMM;
+}
+
+// Scratch of nq_linear_fwd_noalloc: a static device array, so that call never
+// allocates.  Host code only ever uses its per-device address from
+// hipGetSymbolAddress (kept in g_scratch_ptr), never the array's name.
+static __device__ __align__(256) uint8_t scratch[NQ_NOALLOC_SCRATCH_BYTES];
+static constexpr int MAX_DEVICES = 64;
+static void* g_scratch_ptr[MAX_DEVICES] = {};
+static std::mutex g_scratch_mu;
+
 static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
                           void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path,
                           nq::LaunchMarks* marks) {
@@ -192,10 +206,7 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
     uintptr_t y0 = reinterpret_cast<uintptr_t>(y), y1 = y0 + (uintptr_t)B * L->m * yb;
     if (x0 < y1 && y0 < x1) return fail(NQ_ERR_INVALID_ARG, "x and y overlap");
   }
-  if (path == NQ_PATH_AUTO) {
-    if (B <= 4 && nq::dec_plan(L->m, L->n, L->r, B).ok) path = NQ_PATH_DECODE;
-    else path = B <= 16 ? NQ_PATH_GEMV : NQ_PATH_GEMM;
-  }
+  if (path == NQ_PATH_AUTO) path = auto_path(L, B);
   if (path == NQ_PATH_GEMV && B > 16) return fail(NQ_ERR_UNSUPPORTED, "gemv path takes B <= 16 (got %d)", B);
   if (path == NQ_PATH_VALU && B != 1) return fail(NQ_ERR_UNSUPPORTED, "valu path takes B == 1 (got %d)", B);
   if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B).ok)
@@ -251,6 +262,36 @@ nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dty
   nq_status st = fwd_impl(L, x, x_dtype, y, y_dtype, B, workspace, workspace_bytes, stream, path, &marks);
   *n_launches = marks.k > 0 ? marks.k - 1 : 0;
   return st;
+}
+
+nq_status nq_linear_fwd_noalloc(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
+                                int32_t B, nq_stream_t stream) {
+  nq_status st = check_layer(L);
+  if (st) return st;
+  if (B < 0 || B > MAX_BATCH) return fail(NQ_ERR_INVALID_ARG, "batch %d out of range 0..%d", B, MAX_BATCH);
+  if (B == 0) return nq_linear_fwd_path(L, x, x_dtype, y, y_dtype, 0, nullptr, 0, stream, NQ_PATH_AUTO);
+  const size_t need = plan_bytes(L, B, auto_path(L, B));
+  if (need > (size_t)NQ_NOALLOC_SCRATCH_BYTES)
+    return fail(NQ_ERR_WORKSPACE, "this call needs %zu bytes of workspace; the no-allocation scratch holds %zu",
+                need, (size_t)NQ_NOALLOC_SCRATCH_BYTES);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(NQ_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {  // once per device, with that device current
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return nq_linear_fwd_path(L, x, x_dtype, y, y_dtype, B, ptr, (size_t)NQ_NOALLOC_SCRATCH_BYTES, stream,
+                            NQ_PATH_AUTO);
 }
 
 nq_status nq_linear_fwd(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,

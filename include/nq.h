@@ -127,6 +127,23 @@ nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, 
                              int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
                              nq_stream_t stream, int32_t path);
 
+/* Bytes of the static device scratch used by nq_linear_fwd_noalloc. */
+#define NQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* As nq_linear_fwd (automatic path), for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The intermediates live in a static
+ * device array of NQ_NOALLOC_SCRATCH_BYTES (16 MiB) that every GPU the library
+ * runs on holds until the process ends; nothing is allocated or freed.
+ * NQ_ERR_WORKSPACE when the call needs more scratch than that (large prefill
+ * batches: use nq_linear_fwd with a workspace).  All calls on one GPU share
+ * that GPU's scratch: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  The scratch
+ * needs no initial contents.  The first call on a device resolves the
+ * scratch's address on that device (with that device current). */
+nq_status nq_linear_fwd_noalloc(const nq_layer* L, const void* x, int32_t x_dtype, void* y,
+                                int32_t y_dtype, int32_t B, nq_stream_t stream);
+
 /* As nq_linear_fwd_path, and for timing each kernel of the call: records
  * events[k] (hipEvent_t handles created by the caller) on `stream` just before
  * the k-th kernel launch and events[K] after the last of the K launches, for

@@ -120,6 +120,17 @@ def test_fwd_validation_errors(L):
     assert b"overlap" in L.nq_last_error()
 
 
+def test_noalloc_validation_before_any_hip_call(L):
+    big = _layer(m=8192, n=28672, r=5079)
+    # 2048 tokens need far more than the 16 MiB static scratch: refused on the host
+    assert L.nq_linear_fwd_noalloc(ctypes.byref(big), FAKE, nq.NQ_BF16, FAKE + (1 << 30), nq.NQ_BF16, 2048,
+                                   None) == nq.NQ_ERR_WORKSPACE
+    assert b"16777216" in L.nq_last_error()
+    assert L.nq_linear_fwd_noalloc(None, FAKE, nq.NQ_BF16, FAKE, nq.NQ_BF16, 1, None) == nq.NQ_ERR_INVALID_ARG
+    assert L.nq_linear_fwd_noalloc(ctypes.byref(big), FAKE, nq.NQ_BF16, FAKE, nq.NQ_BF16, -1, None) == \
+        nq.NQ_ERR_INVALID_ARG
+
+
 def test_fwd_batch_zero_is_a_no_op(L):
     # valid arguments, nothing to do: returns before any HIP call
     assert fwd(L, _layer(), B=0, x=0, y=0) == nq.NQ_OK
