@@ -55,6 +55,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", default=None, choices=["7b"])
     ap.add_argument("--out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the known-size elementwise kernel used to scale HBM counters")
+    ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
+                    help="print per-kernel tables from rocprofv3 csv output under DIR (no GPU)")
+    ap.add_argument("--make-traffic-file", nargs=5, metavar=("BENCH_JSON", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    default=None, help="write the dominant kernel's counter traffic from --pmc csv dirs (no GPU)")
     return ap.parse_args()
 
 
@@ -69,6 +75,8 @@ def hip_runtime():
                 lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
                 lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
                 lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+                lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+                lib.hipEventQuery.argtypes = [ctypes.c_void_p]
                 return lib
     raise RuntimeError("libamdhip64 is not loaded")
 
@@ -121,7 +129,6 @@ def cpu_info():
 
 
 def chain_spec(shapes, nblocks, bpw):
-    from oracle import nq_oracle  # noqa: F401  (rank rule lives in the library; imported below)
     import binary_rank_gemv_packed_amd as nq
     import synth
     out = []
@@ -216,6 +223,55 @@ def traffic_entry():
     return t
 
 
+KERNEL_NAMES = {2: ["stage1", "stage2"], 3: ["stage1", "mid", "stage2"]}
+
+
+def kernel_durations(nq, stream, spec, layers, xs, ys, ws, path, hold_cycles=100_000_000):
+    """Duration of every kernel of one eager pass over the whole chain: HIP
+    events recorded on `stream` before each launch and after the last one.
+
+    The stream is first held by a GPU spin of hold_cycles clock ticks (40 ms at
+    2.4 GHz) so that the host can queue the whole pass before it runs; then the kernels run back to back as in the graph and no host
+    launch latency leaks into the gaps between events.  Returns {"linear.kernel":
+    [ms per launch]}, {"linear.kernel": (workgroups, threads)} and whether the
+    sleep was still running when the last linear had been queued."""
+    import torch
+    hip = hip_runtime()
+    EV = 4
+    ev = Events(hip, EV * len(spec) + 1)
+    lib = nq.lib()
+    fn = lib.nq_linear_fwd_profiled
+    st = stream.cuda_stream
+    pth = nq.PATHS[path]
+    calls = []
+    for i, (L, x, y) in enumerate(zip(layers, xs, ys)):
+        arr = (ctypes.c_void_p * EV)(*ev.ev[EV * i:EV * i + EV])
+        dims = (ctypes.c_int32 * (2 * EV))()
+        nl = ctypes.c_int32(0)
+        calls.append((L.ref, x.data_ptr(), nq._DT[x.dtype], y.data_ptr(), nq._DT[y.dtype], x.shape[0],
+                      ws.data_ptr(), ws.numel(), st, pth, ctypes.cast(arr, ctypes.c_void_p), EV, ctypes.byref(nl),
+                      ctypes.cast(dims, ctypes.c_void_p), arr, dims, nl))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(hold_cycles)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[-1]), ctypes.c_void_p(st))
+        for c in calls:
+            status = fn(*c[:14])
+            if status != 0:
+                raise nq.NQError(status, lib.nq_last_error().decode())
+        held = hip.hipEventQuery(ctypes.c_void_p(ev.ev[-1])) != 0  # not yet reached: still sleeping
+    torch.cuda.synchronize()
+    per_key, dims_of = {}, {}
+    for i, c in enumerate(calls):
+        nl, dims = c[16].value, c[15]
+        for j, kn in enumerate(KERNEL_NAMES[nl]):
+            key = f"{spec[i][2]}.{kn}"
+            per_key.setdefault(key, []).append(ev.ms(EV * i + j, EV * i + j + 1))
+            dims_of[key] = (dims[2 * j], dims[2 * j + 1])
+    ev.close()
+    return per_key, dims_of, held
+
+
 # ------------------------------------------------------------------ 70B decode chain
 def run_decode70b(args):
     import numpy as np
@@ -281,39 +337,24 @@ def run_decode70b(args):
                         "ok": bool(e <= 2e-3 + er)}
         log(f"[bench] parity {name}: rel L2 {e:.3e} (bf16 rounding alone {er:.3e})")
 
-    # per-kernel durations with HIP events around each launch, block 0's seven linears
+    # per-kernel durations: HIP events around every launch of one more pass over
+    # the whole chain, on the stream the graph ran on (see kernel_durations)
     kernels = {}
     roof = None
     if args.path in ("auto", "decode") and B <= 4:
-        hip = hip_runtime()
-        reps = 20
-        ev = Events(hip, 8 * reps)
-        per_kind = {}
-        with torch.cuda.stream(stream):
-            for li in range(7):
-                _, _, name, m, n, r = spec[li]
-                durs = None
-                launches = 0
-                for k in range(reps):
-                    launches = nq.linear_into_profiled(xs[li], layers[li], ys[li], ws, ev.ev[8 * k:8 * k + 8],
-                                                       args.path)
-                torch.cuda.synchronize()
-                names = ["stage1", "mid", "stage2"] if launches == 3 else ["stage1", "stage2"]
-                durs = {nm: statistics.mean(ev.ms(8 * k + j, 8 * k + j + 1) for k in range(reps))
-                        for j, nm in enumerate(names)}
-                per_kind[name] = (m, n, r, durs)
-        ev.close()
-        counts = {nm: sum(1 for s in spec if s[2] == nm) for nm in per_kind}
+        per_key, dims_of, held = kernel_durations(nq, stream, spec, layers, xs, ys, ws, args.path)
+        log(f"[bench] per-kernel pass: GPU held until all {len(spec)} linears were queued: {held}")
         best = None
-        for name, (m, n, r, durs) in per_kind.items():
-            for kn, d in durs.items():
-                byts = kernel_alg_bytes(kn, m, n, r, B)
-                key = f"{name}.{kn}"
-                kernels[key] = {"us": round(d * 1e3, 3), "alg_bytes": int(byts),
-                                "gbs": round(byts / (d * 1e-3) / 1e9, 1), "per_step": counts[name]}
-                share = d * counts[name]
-                if best is None or share > best[0]:
-                    best = (share, key, byts, d)
+        for key, durs in per_key.items():
+            name, kn = key.split(".")
+            m, n, r = next((s[3], s[4], s[5]) for s in spec if s[2] == name)
+            d = statistics.mean(durs)
+            byts = kernel_alg_bytes(kn, m, n, r, B)
+            kernels[key] = {"us": round(d * 1e3, 3), "alg_bytes": int(byts), "gbs": round(byts / (d * 1e-3) / 1e9, 1),
+                            "per_step": len(durs), "workgroups": dims_of[key][0], "threads": dims_of[key][1]}
+            share = d * len(durs)
+            if best is None or share > best[0]:
+                best = (share, key, byts, d)
         _, key, byts, d = best
         achieved = byts / (d * 1e-3) / 1e9
         tr = traffic_entry()
@@ -322,8 +363,10 @@ def run_decode70b(args):
             traffic = int(tr["traffic_bytes"])
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": key,
-                "us_per_launch": round(d * 1e3, 3), "alg_bytes_per_launch": int(byts)}
-        log(f"[bench] dominant kernel {key}: {d * 1e3:.2f} us/launch, {achieved:.1f} GB/s")
+                "us_per_launch": round(d * 1e3, 3), "alg_bytes_per_launch": int(byts),
+                "launch": {"workgroups": dims_of[key][0], "threads": dims_of[key][1]}}
+        log(f"[bench] dominant kernel {key}: {d * 1e3:.2f} us/launch, {achieved:.1f} GB/s "
+            f"({dims_of[key][0]} workgroups x {dims_of[key][1]} threads)")
 
     out = {
         "metric": "binary low-rank GEMV GB/s (% HBM peak) + tokens/s, 70B-shaped layers, B=1",
@@ -420,13 +463,182 @@ def run_suite7b(args):
                 f.write(json.dumps(row) + "\n")
 
 
+# ------------------------------------------------------------------ profiler summaries
+_DEMANGLED = {}
+
+
+def _demangle(name):
+    if name not in _DEMANGLED:
+        import subprocess
+        try:
+            _DEMANGLED[name] = subprocess.run(["c++filt", name], capture_output=True, text=True,
+                                              check=True).stdout.strip()
+        except (OSError, subprocess.CalledProcessError):
+            _DEMANGLED[name] = name
+        if _DEMANGLED[name].startswith("_Z"):
+            # a name the profiler cut short: keep its last <length><identifier> piece
+            import re
+            best, i = name, 0
+            while True:
+                mt = re.compile(r"(\d+)").search(name, i)
+                if not mt:
+                    break
+                k, j = int(mt.group(1)), mt.end()
+                ident = name[j:j + k]
+                if k and len(ident) == k and (ident[0].isalpha() or ident[0] == "_"):
+                    if "kernel" in ident:
+                        best = ident + "<" + name[j + k:j + k + 12] + "...>"
+                    i = j + k
+                else:
+                    i = mt.start() + 1
+            _DEMANGLED[name] = best
+    return _DEMANGLED[name]
+
+
+def _short_kernel(name):
+    name = name.strip('"')
+    if name.startswith("_Z"):
+        name = _demangle(name)
+    name = name.replace("(anonymous namespace)", "anon")
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    name = name[:cut]
+    return name.replace("nq::anon::", "").replace("nq::", "").replace("at::native::anon::", "").replace(
+        "at::native::", "")
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def trace_table(d):
+    """Per (kernel, workgroups, threads): dispatches and duration statistics
+    from a rocprofv3 --kernel-trace csv directory."""
+    groups = {}
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        key = (_short_kernel(r["Kernel_Name"]), grid // max(wg, 1), wg)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    return groups
+
+
+def counter_table(d):
+    """Per (kernel, workgroups, threads) and counter: the values of every
+    dispatch, from a rocprofv3 --pmc csv directory."""
+    groups = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        wg = int(float(r["Workgroup_Size"]))
+        key = (_short_kernel(r["Kernel_Name"]), int(float(r["Grid_Size"])) // max(wg, 1), wg)
+        groups.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return groups
+
+
+def print_summary(d, top=40):
+    if _csv_rows(d, "kernel_trace.csv"):
+        groups = trace_table(d)
+        total = sum(sum(v) for v in groups.values())
+        print(f"{'kernel':58s} {'wgs':>6s} {'thr':>5s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} "
+              f"{'max us':>9s} {'total %':>8s}")
+        for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]:
+            print(f"{key[0][:58]:58s} {key[1]:6d} {key[2]:5d} {len(v):7d} {statistics.mean(v):9.3f} "
+                  f"{min(v):9.3f} {max(v):9.3f} {100 * sum(v) / total:8.2f}")
+    if _csv_rows(d, "counter_collection.csv"):
+        groups = counter_table(d)
+        names = sorted({c for g in groups.values() for c in g})
+        print(f"{'kernel':58s} {'wgs':>6s} {'thr':>5s} {'calls':>7s} " + " ".join(f"{c:>16s}" for c in names))
+        for key, g in sorted(groups.items(), key=lambda kv: -max(statistics.mean(v) for v in kv[1].values()))[:top]:
+            n = max(len(v) for v in g.values())
+            print(f"{key[0][:58]:58s} {key[1]:6d} {key[2]:5d} {n:7d} " +
+                  " ".join(f"{statistics.mean(g[c]):16.1f}" if c in g else f"{'-':>16s}" for c in names))
+
+
+def copy_calibration():
+    """A plain elementwise kernel of known traffic for scaling the HBM counters:
+    y = -x over 1 GiB of fp32 (reads 1 GiB, writes 1 GiB), three launches."""
+    import torch
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    log("[bench] copy calibration: 3 x neg over 1 GiB fp32 done")
+
+
+KERNEL_PREFIX = {"stage1": "dec_s1_kernel", "mid": "dec_mid_kernel", "stage2": "dec_s2_kernel"}
+
+
+def make_traffic_file(bench_json, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """profiles/decode70b_traffic.json from two --pmc runs of the bench (FETCH_SIZE,
+    WRITE_SIZE) and two of the copy calibration, for the dominant kernel named in
+    the bench's JSON line."""
+    with open(bench_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    roof = json.loads(line)["roofline"]
+    key = roof["kernel"]
+    wgs, thr = roof["launch"]["workgroups"], roof["launch"]["threads"]
+    prefix = KERNEL_PREFIX[key.split(".")[1]]
+
+    def per_dispatch(d, counter, match):
+        vals = []
+        for k, g in counter_table(d).items():
+            if match(k) and counter in g:
+                vals.extend(g[counter])
+        if not vals:
+            raise SystemExit(f"no {counter} rows in {d}")
+        return statistics.median(vals), len(vals)
+
+    big = lambda k: "neg" in k[0] or "elementwise" in k[0] or "vectorized" in k[0]
+    cf, _ = per_dispatch(cfetch_dir, "FETCH_SIZE", big)
+    cw, _ = per_dispatch(cwrite_dir, "WRITE_SIZE", big)
+    ffac, wfac = (1 << 30) / (cf * 1024), (1 << 30) / (cw * 1024)
+    mine = lambda k: k[0].startswith(prefix) and k[1] == wgs and k[2] == thr
+    kf, nf = per_dispatch(fetch_dir, "FETCH_SIZE", mine)
+    kw, nw = per_dispatch(write_dir, "WRITE_SIZE", mine)
+    with open(DEC_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    out = {"kernel": key, "launch": {"workgroups": wgs, "threads": thr}, "source_sha": sha,
+           "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": [nf, nw],
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_factor": round(ffac, 4), "write_factor": round(wfac, 4),
+           "traffic_bytes": int(kf * 1024 * ffac + kw * 1024 * wfac),
+           "alg_bytes_per_launch": roof["alg_bytes_per_launch"]}
+    out["traffic_over_alg"] = round(out["traffic_bytes"] / out["alg_bytes_per_launch"], 4)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.rocprof_summary:
+        print_summary(args.rocprof_summary)
+        return
+    if args.make_traffic_file:
+        make_traffic_file(*args.make_traffic_file)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; --gpus above 1 is not supported "
                                    "(the multi-GPU split is a design note, not built)"}))
         sys.exit(2)
-    if args.suite == "7b":
+    if args.copy_calibration:
+        copy_calibration()
+    elif args.suite == "7b":
         run_suite7b(args)
     else:
         run_decode70b(args)

@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
         "nq_linear_fwd": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
         "nq_linear_fwd_path": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int]),
         "nq_linear_fwd_profiled": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int, vp, c_int,
-                                           ctypes.POINTER(c_int)]),
+                                           ctypes.POINTER(c_int), vp]),
         "nq_linear_fwd_noalloc": (c_int, [P, vp, c_int, vp, c_int, c_int, vp]),
         "nq_bits_per_weight": (ctypes.c_double, [c_int, c_int, c_int, c_int]),
         "nq_rank_for_bits": (c_int, [c_int, c_int, ctypes.c_double, c_int]),
@@ -164,16 +164,20 @@ def linear_into(x: torch.Tensor, layer: Layer, y: torch.Tensor, workspace: torch
 
 
 def linear_into_profiled(x: torch.Tensor, layer: Layer, y: torch.Tensor, workspace: torch.Tensor, events,
-                         path: str = "auto", stream=None) -> int:
+                         path: str = "auto", stream=None):
     """linear_into that records the given HIP events (raw hipEvent_t handles, as
-    ints) around each kernel launch; returns the number of launches."""
+    ints) around each kernel launch.  Returns [(workgroups, threads per
+    workgroup)] of the launches, in order."""
     B = x.shape[0] if x.dim() == 2 else 1
     arr = (ctypes.c_void_p * len(events))(*events)
+    dims = (ctypes.c_int32 * (2 * len(events)))()
     nl = ctypes.c_int32(0)
     _check(lib().nq_linear_fwd_profiled(layer.ref, x.data_ptr(), _DT[x.dtype], y.data_ptr(), _DT[y.dtype], B,
                                         workspace.data_ptr(), workspace.numel(), _stream(stream), PATHS[path],
-                                        ctypes.cast(arr, ctypes.c_void_p), len(events), ctypes.byref(nl)))
-    return nl.value
+                                        ctypes.cast(arr, ctypes.c_void_p), len(events), ctypes.byref(nl),
+                                        ctypes.cast(dims, ctypes.c_void_p)))
+    k = min(nl.value, len(events) - 1)
+    return [(dims[2 * i], dims[2 * i + 1]) for i in range(k)]
 
 
 def linear_noalloc_into(x: torch.Tensor, layer: Layer, y: torch.Tensor, stream=None) -> torch.Tensor:

@@ -233,8 +233,8 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   a.ws_bytes = workspace_bytes;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   a.marks = marks;
-  if (marks && path != NQ_PATH_DECODE)
-    return fail(NQ_ERR_UNSUPPORTED, "timing marks are recorded by the decode path only");
+  if (marks && path != NQ_PATH_DECODE && path != NQ_PATH_GEMM)
+    return fail(NQ_ERR_UNSUPPORTED, "timing marks are recorded by the decode and gemm paths only");
   (void)hipGetLastError();
   hipError_t e;
   switch (path) {
@@ -254,10 +254,12 @@ nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, 
 
 nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
                                  int32_t B, void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path,
-                                 void* const* events, int32_t n_events, int32_t* n_launches) {
+                                 void* const* events, int32_t n_events, int32_t* n_launches,
+                                 int32_t* launch_dims) {
   if (!events || n_events < 1 || !n_launches) return fail(NQ_ERR_INVALID_ARG, "events and n_launches must be given");
   nq::LaunchMarks marks;
   marks.ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  marks.dims = launch_dims;
   marks.n = n_events;
   nq_status st = fwd_impl(L, x, x_dtype, y, y_dtype, B, workspace, workspace_bytes, stream, path, &marks);
   *n_launches = marks.k > 0 ? marks.k - 1 : 0;

@@ -10,18 +10,19 @@
 // block scale).  Column c = b*4 + q of the MFMA carries piece q of batch row b.
 //
 // Launches per forward (all asynchronous, no host synchronisation, nothing
-// that waits on another workgroup; a kernel boundary is the only global sync,
-// because agent-scope fences cost far more on this part than a launch):
-//   s1   : t partials = V^T x' over split column ranges.  Each workgroup first
-//          issues the loads of its row tiles of packed V^T (a ring of
-//          outstanding 1 KiB loads per wave), then encodes x' = s2 * x for its
-//          column range straight into LDS, then streams the row tiles.
+// that waits on another workgroup; a kernel boundary is the only global sync):
+//   s1   : t partials = V^T x' over split column ranges.  Each workgroup issues
+//          the loads of its slice of x and s2, then its packed V^T row tiles
+//          (16 x 1 KiB per wave, all in flight), encodes x' = s2 * x for its
+//          column range into LDS while the weights stream in, then runs the
+//          MFMAs and writes its partial sums.
 //   mid  : (only when the partials are too many to fold into s2) t' = g * sum
 //          of partials -> image of t' (global)
-//   s2   : issues its packed U loads, encodes t' = g * sum of partials into
-//          LDS (or copies the mid image), streams U and writes y = s1 * z.
-// Every prologue issues all of its loads before it uses any, so it costs one
-// memory round trip.
+//   s2   : the same on packed U, with t' = g * sum of partials encoded in the
+//          prologue (or the mid image copied); writes y = s1 * z.
+// Every load of a prologue is issued before the weights and without a branch,
+// so a prologue costs one memory round trip and the encoder never waits for
+// the weight stream.
 #include "nq_common.h"
 #include "nq_internal.h"
 
@@ -34,9 +35,10 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int P = 4;                    // e4m3 pieces per value
-constexpr int DEC_MAX_B = 4;
-constexpr int VMCNT0 = 0x0F70;          // s_waitcnt immediate: vmcnt(0), other counters untouched            // batch rows of the decode path (4 pieces x B <= 16 MFMA columns)
+constexpr int DEC_MAX_B = 4;           // batch rows of the decode path (4 pieces x B <= 16 MFMA columns)
 constexpr int TARGET_WG = 256;          // one workgroup per CU of an MI355X
+constexpr int MIN_WG = 128;
+constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles             // fewest workgroups a stage is cut into (half the CUs)
 constexpr size_t LDS_S1 = 64 * 1024;    // image bytes a stage-1 workgroup may stage
 constexpr size_t LDS_S2 = 64 * 1024;    // image (+ reduction) bytes of a stage-2 workgroup
 
@@ -91,31 +93,33 @@ __device__ __forceinline__ float row16_sum(float v) {
 // b.  The 16 chunks of one (b, ktl) must sit in 16 consecutive active lanes
 // (lane & 15 == j8): four lanes form a 32-value block for the block maximum and
 // the sixteen form the tile sum.
+//
+// The fp4 plane of these columns multiplies the piece by c = 2^cexp (0.5, 1,
+// 2, 2 for planes 0..3), so the MFMA sees piece * 2^(e + cexp): pieces are cut
+// from v * 2^-cexp, with the plane factor folded into each piece's scale and
+// the residual kept in the domain of v.
 __device__ __forceinline__ void encode_chunk(const float (&v)[8], int b, int ktl, int j8, int CW, int B, Img im) {
   const int j = j8 & 3;                                   // sign-bit plane of these 8 columns
-  const float inv_c = j == 0 ? 2.0f : (j == 1 ? 1.0f : 0.5f);
-  const float c = j == 0 ? 0.5f : (j == 1 ? 1.0f : 2.0f);
-  float w[8];
+  const int cexp = j == 0 ? -1 : (j == 1 ? 0 : 1);
   float M = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    w[i] = v[i] * inv_c;
-    M = fmaxf(M, fabsf(w[i]));
-  }
-  M = quad_max(M);
+  for (int i = 0; i < 8; i++) M = fmaxf(M, fabsf(v[i]));
+  M = quad_max(__builtin_ldexpf(M, -cexp));               // block maximum of v * 2^-cexp
   int e0 = 0;
   if (M > 0.0f && M <= 3.4028235e38f) e0 = (__builtin_amdgcn_frexp_expf(M) - 1) - 7;  // max -> [128, 256)
   e0 = e0 < -127 + 4 * (P - 1) ? -127 + 4 * (P - 1) : e0;
-  float orig[8];
+  float w[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) orig[i] = w[i];
+  for (int i = 0; i < 8; i++) w[i] = v[i];
   const int g = (j8 & 7) >> 1;                            // lane group holding these K values
   const int off = 8 * (j8 & 1) + 16 * (j8 >> 3);          // byte offset inside the lane record
   const int kb = j8 >> 2;                                 // 32-value block
+  uint8_t* dst = im.data + (size_t)(ktl * 4 + g) * CW * 32 + off;
+  uint8_t* sdst = im.scale + (size_t)ktl * 4 * CW + kb * CW;
 #pragma unroll
   for (int q = 0; q < P; q++) {
     const int e = e0 - 4 * q;
-    const float sc = __builtin_ldexpf(1.0f, -e), us = __builtin_ldexpf(1.0f, e);
+    const float sc = __builtin_ldexpf(1.0f, -e - cexp), us = __builtin_ldexpf(1.0f, e + cexp);
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[0] * sc, w[1] * sc, 0, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[2] * sc, w[3] * sc, lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(w[4] * sc, w[5] * sc, 0, false);
@@ -132,14 +136,24 @@ __device__ __forceinline__ void encode_chunk(const float (&v)[8], int b, int ktl
     uint2 pk;
     pk.x = (uint32_t)lo;
     pk.y = (uint32_t)hi;
-    *reinterpret_cast<uint2*>(im.data + ((size_t)(ktl * 4 + g) * CW + col) * 32 + off) = pk;
-    if ((j8 & 3) == 0) im.scale[(size_t)ktl * 4 * CW + kb * CW + col] = (uint8_t)(e + 127);
+    *reinterpret_cast<uint2*>(dst + col * 32) = pk;
+    if (j == 0) sdst[col] = (uint8_t)(e + 127);
   }
   float rep = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; i++) rep += orig[i] - w[i];     // represented value, exact
-  rep = row16_sum(rep * c);
+  for (int i = 0; i < 8; i++) rep += v[i] - w[i];         // represented value, exact
+  rep = row16_sum(rep);
   if (j8 == 0) im.sum[(size_t)ktl * B + b] = rep;
+}
+
+// Batch row and column tile of chunk group t (= chunk index / 16) of a range
+// of KL column tiles for BB <= 4 batch rows, without a division.
+template <int BB>
+__device__ __forceinline__ void chunk_pos(int t, int KL, int& b, int& ktl) {
+  b = 0;
+#pragma unroll
+  for (int i = 1; i < BB; i++) b += t >= i * KL ? 1 : 0;
+  ktl = t - b * KL;
 }
 
 // ------------------------------------------------------------------ sources
@@ -157,24 +171,16 @@ template <typename T> struct Raw8 {
   uint4 w[W];
 };
 
-// Loads elements [k, k+8) of p (zero past `end`).  `vec`: p + k is 16-byte
-// aligned and k + 8 <= end, so whole 16-byte words are loaded.
+// Loads the 16-byte word(s) holding elements [k, k+8) of p, k a multiple of 8.
+// Every such word with k < end must be readable (a 16-byte aligned p whose
+// allocation reaches the next 16-byte boundary past end); k >= end reads the
+// first word instead.  Elements at or past `end` are garbage: the encoder masks
+// them.  No branch, so that all loads of a pass are in flight together.
 template <typename T>
-__device__ inline void raw_load(const T* __restrict__ p, int k, int end, bool vec, Raw8<T>& r) {
-  if (vec) {
-    const uint4* q = reinterpret_cast<const uint4*>(p + k);
+__device__ __forceinline__ void raw_words(const T* __restrict__ p, int k, int end, Raw8<T>& r) {
+  const uint4* q = reinterpret_cast<const uint4*>(p + (k < end ? k : 0));
 #pragma unroll
-    for (int i = 0; i < Raw8<T>::W; i++) r.w[i] = q[i];
-  } else {
-    T t[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      T z;
-      __builtin_memset(&z, 0, sizeof(T));
-      t[i] = (k + i < end) ? p[k + i] : z;
-    }
-    __builtin_memcpy(r.w, t, sizeof(t));
-  }
+  for (int i = 0; i < Raw8<T>::W; i++) r.w[i] = q[i];
 }
 
 template <typename T>
@@ -189,105 +195,132 @@ __device__ inline void raw_to_f32(const Raw8<T>& r, float (&v)[8]) {
 // an LDS image, CPT chunks per thread per pass.  Split into the loads of one
 // pass and their encoding, so that a kernel can issue the loads of its first
 // pass before its weight loads and encode while the weights stream in.
-template <typename XT, typename ST>
+template <typename XT, typename ST, int BB>
 struct XPass {
   static constexpr int CPT = 4;
   Raw8<XT> rx[CPT];
   Raw8<ST> rs[CPT];
 
-  __device__ __forceinline__ void load(const XT* __restrict__ x, const ST* __restrict__ s2, int n, int B, int kt0,
-                                       int KL, bool xvec, int base) {
-    const int total = B * KL * 16, nt = blockDim.x;
+  // x rows start every xstride elements, 16-byte aligned, xstride a multiple
+  // of 8; lanes past the last chunk load a copy of it.
+  __device__ __forceinline__ void load(const XT* __restrict__ x, int xstride, const ST* __restrict__ s2, int n,
+                                       int kt0, int KL, int base) {
+    const int total = BB * KL * 16, nt = blockDim.x;
 #pragma unroll
     for (int c = 0; c < CPT; c++) {
       const int ci = base + c * nt + threadIdx.x;
-      if (ci < total) {
-        const int j8 = ci & 15, ktl = (ci >> 4) % KL, b = (ci >> 4) / KL;
-        const int k = (kt0 + ktl) * 128 + 8 * j8;
-        const bool in = k + 8 <= n;
-        raw_load(x + (size_t)b * n, k, n, xvec && in, rx[c]);
-        raw_load(s2, k, n, in, rs[c]);
-      }
+      const int cc = ci < total ? ci : total - 1;
+      int b, ktl;
+      chunk_pos<BB>(cc >> 4, KL, b, ktl);
+      const int k = (kt0 + ktl) * 128 + 8 * (cc & 15);
+      raw_words(x + (size_t)b * xstride, k, n, rx[c]);
+      raw_words(s2, k, n, rs[c]);
     }
   }
 
-  __device__ __forceinline__ void encode(int B, int KL, int CW, int base, Img li) {
-    const int total = B * KL * 16, nt = blockDim.x;
+  __device__ __forceinline__ void encode(int n, int KL, int kt0, int CW, int base, Img li) {
+    const int total = BB * KL * 16, nt = blockDim.x;
 #pragma unroll
     for (int c = 0; c < CPT; c++) {
       const int ci = base + c * nt + threadIdx.x;
       if (ci < total) {  // whole 16-lane groups (total and nt are multiples of 16)
-        const int j8 = ci & 15, ktl = (ci >> 4) % KL, b = (ci >> 4) / KL;
+        const int j8 = ci & 15;
+        int b, ktl;
+        chunk_pos<BB>(ci >> 4, KL, b, ktl);
+        const int k = (kt0 + ktl) * 128 + 8 * j8;
         float xv[8], sv[8], v[8];
         raw_to_f32(rx[c], xv);
         raw_to_f32(rs[c], sv);
 #pragma unroll
         for (int i = 0; i < 8; i++) v[i] = xv[i] * sv[i];
-        encode_chunk(v, b, ktl, j8, CW, B, li);
+        if (k + 8 > n) {  // the ragged end of the input
+#pragma unroll
+          for (int i = 0; i < 8; i++) v[i] = k + i < n ? v[i] : 0.0f;
+        }
+        encode_chunk(v, b, ktl, j8, CW, BB, li);
       }
     }
   }
 };
 
-// Encodes t' = g * (sum over the S1 stage-1 splits) for all KT column tiles
-// into an LDS image, CPT chunks (all splits) per thread per pass; split into
-// loads and encoding like XPass.
-template <typename ST>
+// Encodes t' = g * (sum over the S1 <= SM stage-1 splits) for all KT column
+// tiles into an LDS image, CPT chunks (all splits) per thread per pass; split
+// into loads and encoding like XPass, and branch-free like it (split indices
+// past S1 re-read split S1 - 1 and are left out of the sum).
+template <typename ST, int SM, int BB>
 struct TPass {
-  static constexpr int CPT = 2, SMAX = 4;
-  float4 pv[CPT][SMAX][2];
+  static constexpr int CPT = 2;
+  float4 pv[CPT][SM][2];
   Raw8<ST> rg[CPT];
 
-  __device__ __forceinline__ void load(const float* __restrict__ part, int S1, int B, int Rpad,
+  __device__ __forceinline__ void load(const float* __restrict__ part, int S1, int Rpad,
                                        const ST* __restrict__ g, int r, int KT, int base) {
-    const int total = B * KT * 16, nt = blockDim.x;
+    const int total = BB * KT * 16, nt = blockDim.x;
 #pragma unroll
     for (int c = 0; c < CPT; c++) {
       const int ci = base + c * nt + threadIdx.x;
-      if (ci < total) {
-        const int j8 = ci & 15, kt = (ci >> 4) % KT, b = (ci >> 4) / KT;
-        const int k = kt * 128 + 8 * j8;
-        // k < Rpad implies k + 8 <= Rpad (Rpad is a multiple of 16); values past r are masked at encode
+      const int cc = ci < total ? ci : total - 1;
+      int b, kt;
+      chunk_pos<BB>(cc >> 4, KT, b, kt);
+      const int k = kt * 128 + 8 * (cc & 15);
+      // k < Rpad implies k + 8 <= Rpad (a multiple of 16); values past r are masked at encode
+      const int kp = k < Rpad ? k : 0;
 #pragma unroll
-        for (int s = 0; s < SMAX; s++) {
-          if (s < S1 && k < Rpad) {
-            const float4* pp = reinterpret_cast<const float4*>(part + ((size_t)s * B + b) * Rpad + k);
-            pv[c][s][0] = pp[0];
-            pv[c][s][1] = pp[1];
-          } else {
-            pv[c][s][0] = float4{0.f, 0.f, 0.f, 0.f};
-            pv[c][s][1] = float4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-        raw_load(g, k, r, k + 8 <= r, rg[c]);
+      for (int s = 0; s < SM; s++) {
+        const int ss = s < S1 ? s : S1 - 1;
+        const float4* pp = reinterpret_cast<const float4*>(part + ((size_t)ss * BB + b) * Rpad + kp);
+        pv[c][s][0] = pp[0];
+        pv[c][s][1] = pp[1];
       }
+      raw_words(g, k, r, rg[c]);
     }
   }
 
-  __device__ __forceinline__ void encode(int B, int r, int KT, int CW, int base, Img li) {
-    const int total = B * KT * 16, nt = blockDim.x;
+  __device__ __forceinline__ void encode(int S1, int r, int KT, int CW, int base, Img li) {
+    const int total = BB * KT * 16, nt = blockDim.x;
 #pragma unroll
     for (int c = 0; c < CPT; c++) {
       const int ci = base + c * nt + threadIdx.x;
       if (ci < total) {
-        const int j8 = ci & 15, kt = (ci >> 4) % KT, b = (ci >> 4) / KT;
+        const int j8 = ci & 15;
+        int b, kt;
+        chunk_pos<BB>(ci >> 4, KT, b, kt);
         const int k = kt * 128 + 8 * j8;
         float gv[8], v[8];
         raw_to_f32(rg[c], gv);
         float4 a0 = pv[c][0][0], a1 = pv[c][0][1];
 #pragma unroll
-        for (int s = 1; s < SMAX; s++) {
-          a0.x += pv[c][s][0].x; a0.y += pv[c][s][0].y; a0.z += pv[c][s][0].z; a0.w += pv[c][s][0].w;
-          a1.x += pv[c][s][1].x; a1.y += pv[c][s][1].y; a1.z += pv[c][s][1].z; a1.w += pv[c][s][1].w;
+        for (int s = 1; s < SM; s++) {
+          if (s < S1) {
+            a0.x += pv[c][s][0].x; a0.y += pv[c][s][0].y; a0.z += pv[c][s][0].z; a0.w += pv[c][s][0].w;
+            a1.x += pv[c][s][1].x; a1.y += pv[c][s][1].y; a1.z += pv[c][s][1].z; a1.w += pv[c][s][1].w;
+          }
         }
         const float t[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = (k + i < r) ? t[i] * gv[i] : 0.0f;
-        encode_chunk(v, b, kt, j8, CW, B, li);
+        for (int i = 0; i < 8; i++) v[i] = t[i] * gv[i];
+        if (k + 8 > r) {  // the ragged end of the rank
+#pragma unroll
+          for (int i = 0; i < 8; i++) v[i] = k + i < r ? v[i] : 0.0f;
+        }
+        encode_chunk(v, b, kt, j8, CW, BB, li);
       }
     }
   }
 };
+
+// x copied into rows of xstride (a multiple of 8) elements, zero-padded, for
+// inputs whose rows are not 16-byte aligned.
+template <typename XT>
+__global__ void __launch_bounds__(256) dec_xpad_kernel(const XT* __restrict__ x, int n, int B, int xstride,
+                                                       XT* __restrict__ xp) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * xstride) return;
+  const int b = i / xstride, k = i - b * xstride;
+  XT z;
+  __builtin_memset(&z, 0, sizeof(XT));
+  xp[i] = k < n ? x[(size_t)b * n + k] : z;
+}
 
 // ------------------------------------------------------------------ image kernels
 // Image of g * (sum of stage-1 partials) into global memory, one chunk per
@@ -390,19 +423,23 @@ struct WaveWork {
   int rt0, qa, qb, nfull;
 };
 
+// Issues the wave's RM x QW = 16 quad loads, always 16 and without a branch:
+// a wave with no full quad re-reads the matrix's first 1 KiB (inside the blob
+// for every shape) and ignores it.  With a fixed count the compiler waits for
+// the prologue's loads (issued earlier) without waiting for these.
 template <int RM>
 __device__ __forceinline__ void wave_load(const uint32_t* __restrict__ P, int KT, int RT, WaveWork<RM>& ww, int lane) {
   constexpr int QW = WaveWork<RM>::QW;
   ww.nfull = full_quads(KT, ww.qa, ww.qb);
-  if (ww.nfull == 0) return;  // only the short last quad (read word by word later), or nothing
+  const bool any = ww.nfull > 0;
   const int last = ww.qa + ww.nfull - 1;
 #pragma unroll
   for (int r = 0; r < RM; r++) {
     const int rt = min(ww.rt0 + r, RT - 1);
-    const u4v* qp = reinterpret_cast<const u4v*>(P + (size_t)rt * KT * 64) + lane;
+    const u4v* qp = reinterpret_cast<const u4v*>(P + (any ? (size_t)rt * KT * 64 : 0)) + lane;
 #pragma unroll
     for (int j = 0; j < QW; j++) {
-      const int q = ww.qa + j < last ? ww.qa + j : last;
+      const int q = any ? (ww.qa + j < last ? ww.qa + j : last) : 0;
       ww.w[r][j] = __builtin_nontemporal_load(qp + (size_t)q * 64);
     }
   }
@@ -519,10 +556,9 @@ __device__ __forceinline__ void reduce_parts(float* red, const float (&z)[RM][4]
 struct S1Args {
   const uint32_t* vt;  // packed V^T: rows = rank, columns = inputs
   int RT, KT, KL, RG, KS;
-  const void* x;       // B x n activations
+  const void* x;       // B rows of activations, xstride apart, 16-byte aligned
   const void* s2;      // n input scales
-  int n;
-  bool xvec;           // x rows may be read in aligned 16-byte words
+  int n, xstride;
   int CW, B;
   float* part;
   int Rpad;
@@ -548,27 +584,28 @@ __global__ void __launch_bounds__(512) dec_s1_kernel(S1Args a) {
   const XT* x = reinterpret_cast<const XT*>(a.x);
   const ST* s2 = reinterpret_cast<const ST*>(a.s2);
   const Img li = img_at(lds, KLr, CW);
-  const int per_pass = XPass<XT, ST>::CPT * blockDim.x, total = BB * KLr * 16;
-  XPass<XT, ST> xp;
-  xp.load(x, s2, a.n, BB, kt0, KLr, a.xvec, 0);
-  // the prologue's loads return first: once the weight stream is issued, a
-  // load that misses the caches waits behind it
-  __builtin_amdgcn_s_waitcnt(VMCNT0);
+  const int per_pass = XPass<XT, ST, BB>::CPT * blockDim.x, total = BB * KLr * 16;
+  XPass<XT, ST, BB> xp;
+  // the prologue's loads go out first, then the weight stream; the encoder
+  // waits for the prologue's loads only
+  xp.load(x, a.xstride, s2, a.n, kt0, KLr, 0);
   wave_load<RM>(a.vt, a.KT, a.RT, ww, lane);
-  xp.encode(BB, KLr, CW, 0, li);
+  xp.encode(a.n, KLr, kt0, CW, 0, li);
   for (int base = per_pass; base < total; base += per_pass) {
-    xp.load(x, s2, a.n, BB, kt0, KLr, a.xvec, base);
-    xp.encode(BB, KLr, CW, base, li);
+    xp.load(x, a.xstride, s2, a.n, kt0, KLr, base);
+    xp.encode(a.n, KLr, kt0, CW, base, li);
   }
   __syncthreads();
+  // the tile sums of this wave's range first: they need only LDS, and the
+  // products below wait for the weights anyway
+  float S[4];
+  const int kta = 4 * ww.qa - kt0, ktb = min(kt1, 4 * ww.qb) - kt0;
+  range_sums(li.sum + (size_t)kta * BB, ktb - kta, BB, lane, S);
   const LaneImg<CW> im(li, lane);
   v4f acc[RM];
 #pragma unroll
   for (int r = 0; r < RM; r++) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
   wave_mma<CW, RM>(a.vt, a.KT, a.RT, ww, im, kt0, lane, acc);
-  float S[4];
-  const int kta = 4 * ww.qa - kt0, ktb = min(kt1, 4 * ww.qb) - kt0;
-  range_sums(li.sum + (size_t)kta * BB, ktb - kta, BB, lane, S);
   float z[RM][4];
 #pragma unroll
   for (int r = 0; r < RM; r++) finish_acc(acc[r], S, lane, z[r]);
@@ -595,9 +632,10 @@ struct S2Args {
   void* y;
   int ydt, m;
   int red_off;
+  int s1_off;  // byte offset of the staged output scales in LDS
 };
 
-template <typename ST, bool FUSED, int BB, int RM>
+template <typename ST, bool FUSED, int BB, int RM, int SM>
 __global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
   constexpr int CW = 4 * BB;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -612,41 +650,57 @@ __global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
   const Img li = img_at(lds, a.KT, CW);
   if (FUSED) {
     const ST* g = reinterpret_cast<const ST*>(a.g);
-    const int per_pass = TPass<ST>::CPT * blockDim.x, total = BB * a.KT * 16;
-    TPass<ST> tp;
-    tp.load(a.part, a.S1, BB, a.Rpad1, g, a.r, a.KT, 0);
-    __builtin_amdgcn_s_waitcnt(VMCNT0);  // prologue loads first, then the weight stream
+    const int per_pass = TPass<ST, SM, BB>::CPT * blockDim.x, total = BB * a.KT * 16;
+    TPass<ST, SM, BB> tp;
+    tp.load(a.part, a.S1, a.Rpad1, g, a.r, a.KT, 0);  // prologue loads first, then the weight stream
     wave_load<RM>(a.u, a.KT, a.RT, ww, lane);
-    tp.encode(BB, a.r, a.KT, CW, 0, li);
+    tp.encode(a.S1, a.r, a.KT, CW, 0, li);
     for (int base = per_pass; base < total; base += per_pass) {
-      tp.load(a.part, a.S1, BB, a.Rpad1, g, a.r, a.KT, base);
-      tp.encode(BB, a.r, a.KT, CW, base, li);
+      tp.load(a.part, a.S1, a.Rpad1, g, a.r, a.KT, base);
+      tp.encode(a.S1, a.r, a.KT, CW, base, li);
     }
   } else {
     wave_load<RM>(a.u, a.KT, a.RT, ww, lane);
     copy_image(a.img, a.KT, 0, a.KT, CW, BB, lds);
   }
+  // the output scales of the workgroup's RG * 16 <= 128 rows (two per thread,
+  // clamped, no branch), loaded behind the weights and staged in LDS after the
+  // products, so that the epilogue makes no memory round trip
+  const ST* s1 = reinterpret_cast<const ST*>(a.s1);
+  const int nrows = RG * 16;
+  float s1v[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int t = min((int)threadIdx.x + i * (int)blockDim.x, nrows - 1);
+    s1v[i] = ld_f32(s1, min(ww.rt0 * 16 + t, a.m - 1));
+  }
   __syncthreads();
+  float S[4];  // before the products, as in stage 1
+  const int kta = 4 * ww.qa, ktb = min(a.KT, 4 * ww.qb);
+  range_sums(li.sum + (size_t)kta * BB, ktb - kta, BB, lane, S);
   const LaneImg<CW> im(li, lane);
   v4f acc[RM];
 #pragma unroll
   for (int r = 0; r < RM; r++) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
   wave_mma<CW, RM>(a.u, a.KT, a.RT, ww, im, 0, lane, acc);
-  float S[4];
-  const int kta = 4 * ww.qa, ktb = min(a.KT, 4 * ww.qb);
-  range_sums(li.sum + (size_t)kta * BB, ktb - kta, BB, lane, S);
+  float* s1l = reinterpret_cast<float*>(lds + a.s1_off);
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int t = (int)threadIdx.x + i * (int)blockDim.x;
+    if (t < nrows) s1l[t] = s1v[i];
+  }
+  __syncthreads();
   float z[RM][4];
 #pragma unroll
   for (int r = 0; r < RM; r++) finish_acc(acc[r], S, lane, z[r]);
   float* red = reinterpret_cast<float*>(lds + a.red_off);
-  const ST* s1 = reinterpret_cast<const ST*>(a.s1);
   reduce_parts<RM>(red, z, RG, a.KS, wave, lane, BB, [&](int r, int b, float4 t) {
     const float zz[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
     for (int v = 0; v < 4; v++) {
       const int row = (ww.rt0 + r) * 16 + 4 * (lane >> 4) + v;
       if (row < a.m) {
-        const float yv = ld_f32(s1, row) * zz[v];
+        const float yv = s1l[r * 16 + 4 * (lane >> 4) + v] * zz[v];
         const size_t yi = (size_t)b * a.m + row;
         if (a.ydt == 0) reinterpret_cast<float*>(a.y)[yi] = yv;
         else reinterpret_cast<uint16_t*>(a.y)[yi] = f32_to_bf16(yv);
@@ -660,15 +714,16 @@ __global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
 // ------------------------------------------------------------------ plan
 // Rows per workgroup (RM, a power of two <= 8) and column-part waves (KS <= 8)
 // for a stage of RT row tiles, `splits` column splits, whose waves share
-// `quads` quads.  The largest RM that still gives `groups` row groups and
-// whose 16-quad buffer holds RM x ceil(quads/KS); KS as large as the quads
-// allow (the prologue's parallelism) while the whole grid stays within 8
-// resident waves per CU (2 per SIMD at up to 256 VGPRs), so that it runs in
-// one round.  False if no shape fits.
-static bool pick_shape(int RT, int splits, int quads, int groups, int* RM, int* KS) {
+// `quads` quads.  The largest RM that still gives at least `minwg` workgroups
+// (every workgroup encodes its own copy of its activation range, so fewer,
+// taller workgroups encode less) and whose 16-quad buffer holds RM x
+// ceil(quads/KS); KS as large as the quads allow (the prologue's parallelism)
+// while the whole grid stays within 8 resident waves per CU, so that it runs
+// in one round.  False if no shape fits.
+static bool pick_shape(int RT, int splits, int quads, int minwg, int* RM, int* KS) {
   for (int rm = 8; rm >= 1; rm /= 2) {
     const int wgs = ceil_div(RT, rm) * splits;
-    if (rm > 1 && ceil_div(RT, rm) < groups) continue;
+    if (rm > 1 && wgs < minwg) continue;
     int ks = quads < 8 ? quads : 8;
     const int per_cu = ceil_div(wgs, TARGET_WG);  // workgroups a CU must hold at once
     while (ks > 1 && per_cu * ks > 8) ks--;
@@ -698,7 +753,7 @@ DecPlan dec_plan(int m, int n, int r, int B) {
   if (klmax < 4) return p;
   {
     int rm, ks;
-    if (!pick_shape(p.RT1, 1, 4, 128, &rm, &ks)) return p;  // provisional row groups for the split count
+    if (!pick_shape(p.RT1, 1, 4, MIN_WG, &rm, &ks)) return p;  // provisional row groups for the split count
     const int rowgroups = ceil_div(p.RT1, rm);
     // every stage-2 workgroup reads all S1 partial vectors of t: keep S1 small
     // where the rank is large (the reads are S1 x r x 4 bytes per workgroup)
@@ -709,9 +764,10 @@ DecPlan dec_plan(int m, int n, int r, int B) {
     s = s < 1 ? 1 : s;
     const int s_lds = ceil_div(p.KT1, klmax);
     if (s < s_lds) s = s_lds;
+    if (s == 3) s = 4;  // stage 2 reads 1, 2 or 4 partial vectors
     p.KL1 = 4 * ceil_div(ceil_div(p.KT1, s), 4);
     p.S1 = ceil_div(p.KT1, p.KL1);
-    if (!pick_shape(p.RT1, p.S1, ceil_div(p.KL1, 4), ceil_div(TARGET_WG, p.S1), &p.RG1, &p.KS1)) return p;
+    if (!pick_shape(p.RT1, p.S1, ceil_div(p.KL1, 4), MIN_WG, &p.RG1, &p.KS1)) return p;
   }
   p.QM1 = ceil_div(ceil_div(p.KL1, 4), p.KS1);
   p.Rpad1 = p.RT1 * 16;
@@ -721,13 +777,13 @@ DecPlan dec_plan(int m, int n, int r, int B) {
   p.RT2 = ceil_div(m, 16);
   p.KT2 = ceil_div(r, 128);
   const int quads2 = ceil_div(p.KT2, 4);
-  if (!pick_shape(p.RT2, 1, quads2, TARGET_WG, &p.RG2, &p.KS2)) return p;
+  if (!pick_shape(p.RT2, 1, quads2, MIN_WG, &p.RG2, &p.KS2)) return p;
   {
     // the prologue encodes B x KT2 x 16 chunks, 2 per thread per pass: prefer
     // a shape that does it in one pass, if that keeps >= 3/4 of the CUs busy
     const int chunks = B * p.KT2 * 16;
     int rm, ks;
-    if (chunks > 2 * 64 * p.KS2 && pick_shape(p.RT2, 1, quads2, TARGET_WG * 3 / 4, &rm, &ks) &&
+    if (chunks > 2 * 64 * p.KS2 && pick_shape(p.RT2, 1, quads2, MIN_WG * 3 / 4, &rm, &ks) &&
         chunks <= 2 * 64 * ks) {
       p.RG2 = rm;
       p.KS2 = ks;
@@ -735,9 +791,9 @@ DecPlan dec_plan(int m, int n, int r, int B) {
   }
   p.QM2 = ceil_div(quads2, p.KS2);
   p.red2 = align_up((size_t)p.KT2 * tb, 16);
-  p.lds2 = p.red2 + red_bytes;
+  p.lds2 = p.red2 + red_bytes + S1_LDS_BYTES;
   if (p.lds2 > LDS_S2) return p;
-  p.fused_mid = p.S1 <= 4 && p.S1 * B <= 4;
+  p.fused_mid = p.S1 * B <= 4 && p.S1 != 3;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -747,9 +803,20 @@ DecPlan dec_plan(int m, int n, int r, int B) {
   p.off_img1 = 0;
   p.off_part = take((size_t)p.S1 * B * p.Rpad1 * 4);
   p.off_img2 = take(p.fused_mid ? 0 : (size_t)p.KT2 * tb);
+  p.off_xpad = take((size_t)B * align_up(n, 8) * 4);
   p.bytes = o;
   p.ok = true;
   return p;
+}
+
+template <typename ST, bool FUSED, int BB, int SM>
+static void launch_s2(int RG, dim3 g, dim3 b, size_t lds, hipStream_t st, const S2Args& k) {
+  switch (RG) {
+    case 8: hipLaunchKernelGGL((dec_s2_kernel<ST, FUSED, BB, 8, SM>), g, b, lds, st, k); break;
+    case 4: hipLaunchKernelGGL((dec_s2_kernel<ST, FUSED, BB, 4, SM>), g, b, lds, st, k); break;
+    case 2: hipLaunchKernelGGL((dec_s2_kernel<ST, FUSED, BB, 2, SM>), g, b, lds, st, k); break;
+    default: hipLaunchKernelGGL((dec_s2_kernel<ST, FUSED, BB, 1, SM>), g, b, lds, st, k); break;
+  }
 }
 
 template <typename XT, typename ST, int BB>
@@ -765,11 +832,22 @@ static hipError_t dec_forward_t(const FwdArgs& a, const DecPlan& p) {
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
   uint8_t* img2 = a.ws + p.off_img2;
   const bool xvec = (a.n % 8 == 0) && (reinterpret_cast<uintptr_t>(a.x) % 16 == 0);
+  const void* x = a.x;
+  int xstride = a.n;
+  if (!xvec) {  // rows not 16-byte aligned: an aligned, zero-padded copy first
+    xstride = align_up(a.n, 8);
+    XT* xp = reinterpret_cast<XT*>(a.ws + p.off_xpad);
+    const int tot = a.B * xstride;
+    mark(a, dim3(ceil_div(tot, 256)), dim3(256));
+    hipLaunchKernelGGL((dec_xpad_kernel<XT>), dim3(ceil_div(tot, 256)), dim3(256), 0, st,
+                       reinterpret_cast<const XT*>(a.x), a.n, a.B, xstride, xp);
+    x = xp;
+  }
 
-  S1Args k1{Vt, p.RT1, p.KT1, p.KL1, p.RG1, p.KS1, a.x, s2, a.n, xvec, p.CW, a.B, part, p.Rpad1, (int)p.red1};
-  mark(a);
+  S1Args k1{Vt, p.RT1, p.KT1, p.KL1, p.RG1, p.KS1, x, s2, a.n, xstride, p.CW, a.B, part, p.Rpad1, (int)p.red1};
   {
     dim3 g1(ceil_div(p.RT1, p.RG1), p.S1), b1(64 * p.KS1);
+    mark(a, g1, b1);
     switch (p.RG1) {
       case 8: hipLaunchKernelGGL((dec_s1_kernel<XT, ST, BB, 8>), g1, b1, p.lds1, st, k1); break;
       case 4: hipLaunchKernelGGL((dec_s1_kernel<XT, ST, BB, 4>), g1, b1, p.lds1, st, k1); break;
@@ -779,31 +857,22 @@ static hipError_t dec_forward_t(const FwdArgs& a, const DecPlan& p) {
   }
   if (!p.fused_mid) {
     const int c2 = a.B * p.KT2 * 16;
-    mark(a);
+    mark(a, dim3(ceil_div(c2, 256)), dim3(256));
     hipLaunchKernelGGL((dec_mid_kernel<ST>), dim3(ceil_div(c2, 256)), dim3(256), 0, st, part, p.S1, p.Rpad1, g,
                        a.r, a.B, p.KT2, p.CW, img2);
   }
   S2Args k2{U, p.RT2, p.KT2, p.RG2, p.KS2, p.fused_mid ? nullptr : img2, part, p.S1, p.Rpad1, a.r, g, p.CW, a.B,
-            s1, a.scale_dtype, a.y, a.y_dtype == 0 ? 0 : 2, a.m, (int)p.red2};
+            s1, a.scale_dtype, a.y, a.y_dtype == 0 ? 0 : 2, a.m, (int)p.red2, (int)(p.lds2 - S1_LDS_BYTES)};
   dim3 g2(ceil_div(p.RT2, p.RG2)), b2(64 * p.KS2);
-  mark(a);
-#define NQ_S2(F, RM) hipLaunchKernelGGL((dec_s2_kernel<ST, F, BB, RM>), g2, b2, p.lds2, st, k2)
+  mark(a, g2, b2);
   if (p.fused_mid) {
-    switch (p.RG2) {
-      case 8: NQ_S2(true, 8); break;
-      case 4: NQ_S2(true, 4); break;
-      case 2: NQ_S2(true, 2); break;
-      default: NQ_S2(true, 1); break;
-    }
+    // splits read by the prologue: 1, 2 or 4 (S1 * B <= 4)
+    if (p.S1 == 1) launch_s2<ST, true, BB, 1>(p.RG2, g2, b2, p.lds2, st, k2);
+    else if (p.S1 == 2) launch_s2<ST, true, BB, (BB <= 2 ? 2 : 1)>(p.RG2, g2, b2, p.lds2, st, k2);
+    else launch_s2<ST, true, BB, (BB == 1 ? 4 : 1)>(p.RG2, g2, b2, p.lds2, st, k2);
   } else {
-    switch (p.RG2) {
-      case 8: NQ_S2(false, 8); break;
-      case 4: NQ_S2(false, 4); break;
-      case 2: NQ_S2(false, 2); break;
-      default: NQ_S2(false, 1); break;
-    }
+    launch_s2<ST, false, BB, 1>(p.RG2, g2, b2, p.lds2, st, k2);
   }
-#undef NQ_S2
   mark(a);
   return hipGetLastError();
 }

@@ -265,18 +265,18 @@ static hipError_t gemm_forward_t(const FwdArgs& a, const GemmPlan& p) {
   hipStream_t st = a.stream;
   const int B = a.B;
 
-  mark(a);
+  mark(a, dim3(B), dim3(256));
   hipLaunchKernelGGL((row_to_f16_kernel<XT, ST>), dim3(B), dim3(256), 0, st, reinterpret_cast<const XT*>(a.x),
                      (size_t)a.n, s2, a.n, p.KT1 * 128, x16, xexp);
   GemmArgs g1{x16, xexp, Vt, B, a.r, p.KT1, t32, (size_t)a.r, nullptr, 0, ceil_div(B, BM), ceil_div(a.r, BN)};
-  mark(a);
+  mark(a, dim3(8 * ceil_div(g1.MB * g1.NB, 8)), dim3(256));
   hipLaunchKernelGGL((gemm_kernel<0, ST>), dim3(8 * ceil_div(g1.MB * g1.NB, 8)), dim3(256), 0, st, g1);
-  mark(a);
+  mark(a, dim3(B), dim3(256));
   hipLaunchKernelGGL((row_to_f16_kernel<float, ST>), dim3(B), dim3(256), 0, st, t32, (size_t)a.r, g, a.r,
                      p.KT2 * 128, t16, texp);
   GemmArgs g2{t16, texp, U, B, a.m, p.KT2, a.y, (size_t)a.m, s1, a.y_dtype == 0 ? 0 : 2, ceil_div(B, BM),
               ceil_div(a.m, BN)};
-  mark(a);
+  mark(a, dim3(8 * ceil_div(g2.MB * g2.NB, 8)), dim3(256));
   hipLaunchKernelGGL((gemm_kernel<1, ST>), dim3(8 * ceil_div(g2.MB * g2.NB, 8)), dim3(256), 0, st, g2);
   mark(a);
   return hipGetLastError();

@@ -17,10 +17,15 @@ hipError_t launch_unpack(const uint32_t* in, int R, int C, long long ld_row, lon
 // k-th kernel launch of a forward, and one more after the last launch.
 struct LaunchMarks {
   hipEvent_t* ev = nullptr;
+  int32_t* dims = nullptr;  // per launch: workgroups, threads per workgroup
   int n = 0;
   int k = 0;
-  void mark(hipStream_t s) {
+  void mark(hipStream_t s, dim3 grid, dim3 block) {
     if (ev && k < n) hipEventRecord(ev[k], s);
+    if (dims && k < n - 1) {
+      dims[2 * k] = (int32_t)(grid.x * grid.y * grid.z);
+      dims[2 * k + 1] = (int32_t)(block.x * block.y * block.z);
+    }
     k++;
   }
 };
@@ -37,8 +42,10 @@ struct FwdArgs {
   LaunchMarks* marks = nullptr;  // null: no timing marks
 };
 
-inline void mark(const FwdArgs& a) {
-  if (a.marks) a.marks->mark(a.stream);
+// Before each launch (with its grid and block) and once after the last one
+// (no arguments).
+inline void mark(const FwdArgs& a, dim3 grid = dim3(0, 0, 0), dim3 block = dim3(0, 0, 0)) {
+  if (a.marks) a.marks->mark(a.stream, grid, block);
 }
 
 // Work split of one sign-matrix product over wavefronts: each wave handles one
@@ -73,7 +80,7 @@ struct DecPlan {
   int RT2, KT2, RG2, KS2;
   int QM1, QM2;  // most quads one wave of stage 1 / stage 2 streams per row tile
   size_t lds1, lds2, red1, red2;
-  size_t off_img1, off_part, off_img2;
+  size_t off_img1, off_part, off_img2, off_xpad;
   size_t bytes;
 };
 DecPlan dec_plan(int m, int n, int r, int B);

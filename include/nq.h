@@ -147,14 +147,18 @@ nq_status nq_linear_fwd_noalloc(const nq_layer* L, const void* x, int32_t x_dtyp
 /* As nq_linear_fwd_path, and for timing each kernel of the call: records
  * events[k] (hipEvent_t handles created by the caller) on `stream` just before
  * the k-th kernel launch and events[K] after the last of the K launches, for
- * the first n_events of them; *n_launches receives K.  Only NQ_PATH_DECODE
- * (or AUTO resolving to it) records marks; other paths return
- * NQ_ERR_UNSUPPORTED.  The launches are those of nq_linear_fwd_path, in order
- * (decode: activation image, stage 1, [mid image,] stage 2). */
+ * the first n_events of them; *n_launches receives K.  If launch_dims is not
+ * NULL it receives, for each of the first n_events - 1 launches, the number of
+ * workgroups and the threads per workgroup (2 int32 per launch), so that a
+ * profiler's dispatch records can be matched to the launches.  Only
+ * NQ_PATH_DECODE and NQ_PATH_GEMM (or AUTO resolving to them) record marks;
+ * other paths return NQ_ERR_UNSUPPORTED.  The launches are those of
+ * nq_linear_fwd_path, in order (decode: stage 1, [mid image,] stage 2; gemm:
+ * x image, product with V^T, t image, product with U). */
 nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dtype, void* y,
                                  int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
                                  nq_stream_t stream, int32_t path, void* const* events,
-                                 int32_t n_events, int32_t* n_launches);
+                                 int32_t n_events, int32_t* n_launches, int32_t* launch_dims);
 
 /* Average bits per original weight: (r(m+n) + scale_bits (m+n+r)) / (m n)
  * (hardwired.dev, sections "Jak NanoQuant funguje" and 'Co znamena
