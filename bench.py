@@ -4,17 +4,19 @@
 Default workload: Llama-2-70B-shaped decode, 80 blocks x {q, k, v, o, gate, up,
 down} linears at 0.8 bits/weight (ranks from the storage rule r(m+n) bits +
 16-bit scales), batch 1, bf16 activations and outputs, fp16 scales.  Every layer
-has its own seeded random signs and scales and every linear its own seeded
-input (no attention, norm or embedding between them).  One step = the 560
-linears in block order on one stream, each finished before the next starts,
-captured once as a HIP graph and replayed.
+has its own seeded random signs and scales (no attention, norm or embedding
+between the linears).  One step = the 80 blocks in order, each as its four
+shared-input groups q+k+v, o, gate+up, down (nq_linear_fwd_group: two launches
+per group), each finished before the next starts, captured once as a HIP graph
+and replayed; the same layers run one linear at a time (560 linears) are timed
+too, for comparison (`unfused_chain`; --unfused makes that the headline).
 
 Prints one JSON line.  `value` is algorithmic GB/s over the whole step: per
-linear r(m+n)/8 sign bytes + 2(m+n+r) scale bytes + 2Bn x bytes + 2Bm y bytes.
-`roofline` is for the dominant kernel (largest share of the step), timed with
-HIP events around each of its launches on the stream it runs on.  After the
-timed region one layer of every distinct shape of block 0 is checked against
-the fp64 oracle on the host (`parity`).
+linear r(m+n)/8 sign bytes + 2(m+n+r) scale bytes + 2Bm y bytes, plus 2Bn x
+bytes per group.  `roofline` is for the dominant kernel (largest share of the
+step), timed with HIP events around each of its launches on the stream it runs
+on.  After the timed region one layer of every distinct shape of block 0 is
+checked against the fp64 oracle on the host (`parity`).
 
   python bench.py [--steps K --warmup W]           70B decode chain (the metric)
   python bench.py --suite 7b --out FILE            7B shapes, B in {1,2,4,8,16}, 0.55/0.8/1.0 bpw:
@@ -53,6 +55,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemv", "valu"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="time the 560 linears one by one (no layer groups)")
     ap.add_argument("--suite", default=None, choices=["7b"])
     ap.add_argument("--out", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -102,17 +105,6 @@ class Events:
 
 def alg_bytes(m, n, r, B, xb=2, yb=2, sb=2):
     return r * (m + n) / 8 + sb * (m + n + r) + B * n * xb + B * m * yb
-
-
-def kernel_alg_bytes(kind, m, n, r, B, xb=2, yb=2, sb=2):
-    """Algorithmic bytes each kernel of the decode path owns: stage 1 reads x,
-    s2 and the packed V^T bits; stage 2 the packed U bits, s1 and g and writes
-    y (intermediates such as the partial sums of t are not counted)."""
-    if kind == "stage1":
-        return r * n / 8 + B * n * xb + sb * n
-    if kind == "mid":
-        return 0.0
-    return r * m / 8 + sb * (m + r) + B * m * yb
 
 
 def cpu_info():
@@ -224,57 +216,132 @@ def traffic_entry():
 
 
 KERNEL_NAMES = {2: ["stage1", "stage2"], 3: ["stage1", "mid", "stage2"]}
+# the linears of a block that read the same input, in block order
+GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
 
 
-def kernel_durations(nq, stream, spec, layers, xs, ys, ws, path, hold_cycles=100_000_000):
+def make_units(spec, fused):
+    """The chain as a list of (name, [linear indices]) in step order: every
+    linear alone, or the shared-input groups of each block."""
+    if not fused:
+        return [(s[2], [i]) for i, s in enumerate(spec)]
+    units = []
+    by_block = {}
+    for i, s in enumerate(spec):
+        by_block.setdefault(s[0], {})[s[2]] = i
+    for blk in sorted(by_block):
+        for gname, members in GROUPS:
+            units.append((gname, [by_block[blk][nm] for nm in members]))
+    return units
+
+
+def unit_call(nq, units, layers, xs, ys, ws, path):
+    """Launches of one pass over the units (x of a group = x of its first linear)."""
+    def step():
+        for _, idx in units:
+            if len(idx) == 1:
+                nq.linear_into(xs[idx[0]], layers[idx[0]], ys[idx[0]], ws, path)
+            else:
+                nq.linear_group_into(xs[idx[0]], [layers[i] for i in idx], [ys[i] for i in idx], ws)
+    return step
+
+
+def unit_alg_bytes(kind, spec, idx, B):
+    """Algorithmic bytes of one kernel of a unit (x read once per unit): stage 1
+    reads x, s2 and packed V^T; stage 2 packed U, s1 and g and writes y."""
+    n = spec[idx[0]][4]
+    if kind == "stage1":
+        return 2 * B * n + sum(spec[i][5] * n / 8 + 2 * n for i in idx)
+    if kind == "mid":
+        return 0.0
+    return sum(spec[i][5] * spec[i][3] / 8 + 2 * (spec[i][3] + spec[i][5]) + 2 * B * spec[i][3] for i in idx)
+
+
+def kernel_durations(nq, stream, units, layers, xs, ys, ws, path, hold_cycles=100_000_000):
     """Duration of every kernel of one eager pass over the whole chain: HIP
     events recorded on `stream` before each launch and after the last one.
 
     The stream is first held by a GPU spin of hold_cycles clock ticks (40 ms at
-    2.4 GHz) so that the host can queue the whole pass before it runs; then the kernels run back to back as in the graph and no host
-    launch latency leaks into the gaps between events.  Returns {"linear.kernel":
-    [ms per launch]}, {"linear.kernel": (workgroups, threads)} and whether the
-    sleep was still running when the last linear had been queued."""
+    2.4 GHz) so that the host can queue the whole pass before it runs; then the
+    kernels run back to back as in the graph and no host launch latency leaks
+    into the gaps between events.  Returns {"unit.kernel": [ms per launch]},
+    {"unit.kernel": (workgroups, threads)} and whether the spin was still
+    running when the last unit had been queued."""
     import torch
     hip = hip_runtime()
     EV = 4
-    ev = Events(hip, EV * len(spec) + 1)
+    ev = Events(hip, EV * len(units) + 1)
     lib = nq.lib()
-    fn = lib.nq_linear_fwd_profiled
     st = stream.cuda_stream
     pth = nq.PATHS[path]
     calls = []
-    for i, (L, x, y) in enumerate(zip(layers, xs, ys)):
-        arr = (ctypes.c_void_p * EV)(*ev.ev[EV * i:EV * i + EV])
+    for u, (name, idx) in enumerate(units):
+        arr = (ctypes.c_void_p * EV)(*ev.ev[EV * u:EV * u + EV])
         dims = (ctypes.c_int32 * (2 * EV))()
         nl = ctypes.c_int32(0)
-        calls.append((L.ref, x.data_ptr(), nq._DT[x.dtype], y.data_ptr(), nq._DT[y.dtype], x.shape[0],
-                      ws.data_ptr(), ws.numel(), st, pth, ctypes.cast(arr, ctypes.c_void_p), EV, ctypes.byref(nl),
-                      ctypes.cast(dims, ctypes.c_void_p), arr, dims, nl))
+        x = xs[idx[0]]
+        if len(idx) == 1:
+            L, y = layers[idx[0]], ys[idx[0]]
+            args = (L.ref, x.data_ptr(), nq._DT[x.dtype], y.data_ptr(), nq._DT[y.dtype], x.shape[0],
+                    ws.data_ptr(), ws.numel(), st, pth, ctypes.cast(arr, ctypes.c_void_p), EV, ctypes.byref(nl),
+                    ctypes.cast(dims, ctypes.c_void_p))
+            calls.append((lib.nq_linear_fwd_profiled, args, (arr, dims, nl)))
+        else:
+            refs, yp = nq._group_arrays([layers[i] for i in idx], [ys[i] for i in idx])
+            args = (ctypes.cast(refs, ctypes.c_void_p), len(idx), x.data_ptr(), nq._DT[x.dtype],
+                    ctypes.cast(yp, ctypes.c_void_p), nq._DT[ys[idx[0]].dtype], x.shape[0], ws.data_ptr(),
+                    ws.numel(), st, ctypes.cast(arr, ctypes.c_void_p), EV, ctypes.byref(nl),
+                    ctypes.cast(dims, ctypes.c_void_p))
+            calls.append((lib.nq_linear_fwd_group_profiled, args, (arr, dims, nl, refs, yp)))
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         torch.cuda._sleep(hold_cycles)
         hip.hipEventRecord(ctypes.c_void_p(ev.ev[-1]), ctypes.c_void_p(st))
-        for c in calls:
-            status = fn(*c[:14])
+        for fn, args, _ in calls:
+            status = fn(*args)
             if status != 0:
                 raise nq.NQError(status, lib.nq_last_error().decode())
-        held = hip.hipEventQuery(ctypes.c_void_p(ev.ev[-1])) != 0  # not yet reached: still sleeping
+        held = hip.hipEventQuery(ctypes.c_void_p(ev.ev[-1])) != 0  # not yet reached: still spinning
     torch.cuda.synchronize()
     per_key, dims_of = {}, {}
-    for i, c in enumerate(calls):
-        nl, dims = c[16].value, c[15]
+    for u, (fn, args, keep) in enumerate(calls):
+        dims, nl = keep[1], keep[2].value
         for j, kn in enumerate(KERNEL_NAMES[nl]):
-            key = f"{spec[i][2]}.{kn}"
-            per_key.setdefault(key, []).append(ev.ms(EV * i + j, EV * i + j + 1))
+            key = f"{units[u][0]}.{kn}"
+            per_key.setdefault(key, []).append(ev.ms(EV * u + j, EV * u + j + 1))
             dims_of[key] = (dims[2 * j], dims[2 * j + 1])
     ev.close()
     return per_key, dims_of, held
 
 
 # ------------------------------------------------------------------ 70B decode chain
+def time_graph(torch, stream, step, warmup, steps):
+    """Captures one step as a HIP graph and times `steps` replays on `stream`
+    with events on that stream; returns (ms per step, wall ms per step)."""
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
 def run_decode70b(args):
-    import numpy as np
     import torch
     import binary_rank_gemv_packed_amd as nq
     import synth
@@ -282,6 +349,7 @@ def run_decode70b(args):
     dev = "cuda:0"
     B = args.batch
     spec = chain_spec(synth.LLAMA70B, 80, args.bpw)
+    fused = not args.unfused and B <= 4 and args.path == "auto"
     check_ids = {0: "q", 1: "k", 4: "gate", 6: "down"}  # one linear per distinct shape of block 0
     layers, xs, ys, hosts = [], [], [], {}
     t0 = time.time()
@@ -294,62 +362,54 @@ def run_decode70b(args):
         if keep:
             hosts[i] = host
     log(f"[bench] generated and packed {len(spec)} layers in {time.time() - t0:.1f}s")
+    units = make_units(spec, fused)
     ws_bytes = max(nq.workspace_bytes(L, B, args.path) for L in layers)
+    for _, idx in units:
+        if len(idx) > 1:
+            ws_bytes = max(ws_bytes, nq.workspace_bytes_group([layers[i] for i in idx], B))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream()
 
-    def step():
-        for L, x, y in zip(layers, xs, ys):
-            nq.linear_into(x, L, y, ws, args.path)
-
-    with torch.cuda.stream(stream):
-        step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        step()
-    torch.cuda.synchronize()
-    # replays run on `stream`, and the events are recorded on that same stream
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
-    step_bytes = sum(alg_bytes(m, n, r, B) for (_, _, _, m, n, r) in spec)
+    ms, wall = time_graph(torch, stream, unit_call(nq, units, layers, xs, ys, ws, args.path), args.warmup,
+                          args.steps)
+    log(f"[bench] {'fused' if fused else 'unfused'} chain, {len(units)} units, {args.steps} steps: "
+        f"{ms:.4f} ms/step (events), wall {wall:.4f} ms/step")
+    step_bytes = sum(unit_alg_bytes("stage1", spec, idx, B) + unit_alg_bytes("stage2", spec, idx, B)
+                     for _, idx in units)
     gbs = step_bytes / (ms * 1e-3) / 1e9
 
-    # parity of the timed chain's own outputs (last replay), one linear per distinct shape
+    # parity of the timed chain's own outputs (last replay), one linear per
+    # distinct shape; a group member's input is its group's (first linear's) x
+    leader = {i: idx[0] for _, idx in units for i in idx}
     parity = {}
     for i, host in hosts.items():
+        if leader[i] != i:
+            host = dict(host, x=xs[leader[i]].float().cpu().numpy())
         e, er = oracle_check(host, ys[i].float().cpu().numpy())
         name = spec[i][2]
         parity[name] = {"rel_l2": float(f"{e:.3e}"), "bf16_rounding_rel_l2": float(f"{er:.3e}"),
                         "ok": bool(e <= 2e-3 + er)}
         log(f"[bench] parity {name}: rel L2 {e:.3e} (bf16 rounding alone {er:.3e})")
 
+    unfused_ms = None
+    if fused:  # the per-linear chain on the same layers, for comparison
+        unfused_ms, _ = time_graph(torch, stream, unit_call(nq, make_units(spec, False), layers, xs, ys, ws,
+                                                            args.path), args.warmup, args.steps)
+        log(f"[bench] unfused chain (560 linears one by one): {unfused_ms:.4f} ms/step")
+
     # per-kernel durations: HIP events around every launch of one more pass over
     # the whole chain, on the stream the graph ran on (see kernel_durations)
     kernels = {}
     roof = None
     if args.path in ("auto", "decode") and B <= 4:
-        per_key, dims_of, held = kernel_durations(nq, stream, spec, layers, xs, ys, ws, args.path)
-        log(f"[bench] per-kernel pass: GPU held until all {len(spec)} linears were queued: {held}")
+        per_key, dims_of, held = kernel_durations(nq, stream, units, layers, xs, ys, ws, args.path)
+        log(f"[bench] per-kernel pass: GPU held until all {len(units)} units were queued: {held}")
+        unit_idx = {name: idx for name, idx in units}
         best = None
         for key, durs in per_key.items():
-            name, kn = key.split(".")
-            m, n, r = next((s[3], s[4], s[5]) for s in spec if s[2] == name)
+            uname, kn = key.split(".")
             d = statistics.mean(durs)
-            byts = kernel_alg_bytes(kn, m, n, r, B)
+            byts = unit_alg_bytes(kn, spec, unit_idx[uname], B)
             kernels[key] = {"us": round(d * 1e3, 3), "alg_bytes": int(byts), "gbs": round(byts / (d * 1e-3) / 1e9, 1),
                             "per_step": len(durs), "workgroups": dims_of[key][0], "threads": dims_of[key][1]}
             share = d * len(durs)
@@ -388,10 +448,15 @@ def run_decode70b(args):
             "blocks": 80, "linears_per_block": 7, "batch": B, "bits_per_weight": args.bpw,
             "ranks": {s[2]: s[5] for s in spec[:7]}, "x_dtype": "bf16", "y_dtype": "bf16", "scale_dtype": "fp16",
             "path": args.path, "graph": True, "bytes_per_step": int(step_bytes),
+            "chain": ("fused groups per block: q+k+v, o, gate+up, down (2 launches each)" if fused else
+                      "560 linears one by one"),
         },
         "parity": parity,
         "kernels": kernels,
     }
+    if unfused_ms is not None:
+        out["unfused_chain"] = {"ms_per_step": round(unfused_ms, 5), "tokens_per_s": round(B / (unfused_ms * 1e-3), 2),
+                                "speedup_of_fused": round(unfused_ms / ms, 3)}
     if roof is not None:
         out["roofline"] = roof
     if not args.no_cpu_baseline:
@@ -580,7 +645,7 @@ def copy_calibration():
     log("[bench] copy calibration: 3 x neg over 1 GiB fp32 done")
 
 
-KERNEL_PREFIX = {"stage1": "dec_s1_kernel", "mid": "dec_mid_kernel", "stage2": "dec_s2_kernel"}
+KERNEL_PREFIX = {"stage1": "dec_s1", "mid": "dec_mid_kernel", "stage2": "dec_s2"}
 
 
 def make_traffic_file(bench_json, fetch_dir, write_dir, cfetch_dir, cwrite_dir):

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libnq.so")
 NQ_OK, NQ_ERR_INVALID_ARG, NQ_ERR_NOT_PM1, NQ_ERR_WORKSPACE, NQ_ERR_UNSUPPORTED, NQ_ERR_HIP, NQ_ERR_INTERNAL = \
     0, -1, -2, -3, -4, -5, -6
 NQ_F32, NQ_F16, NQ_BF16 = 0, 1, 2
+NQ_GROUP_MAX = 4  # layers per group call (include/nq.h)
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "valu": 3, "decode": 4}
 
 _DT = {torch.float32: NQ_F32, torch.float16: NQ_F16, torch.bfloat16: NQ_BF16}
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
         "nq_linear_fwd_profiled": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp, c_int, vp, c_int,
                                            ctypes.POINTER(c_int), vp]),
         "nq_linear_fwd_noalloc": (c_int, [P, vp, c_int, vp, c_int, c_int, vp]),
+        "nq_workspace_bytes_group": (c_size, [vp, c_int, c_int]),
+        "nq_linear_fwd_group": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
+        "nq_linear_fwd_group_profiled": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp, vp, c_int,
+                                                 ctypes.POINTER(c_int), vp]),
         "nq_bits_per_weight": (ctypes.c_double, [c_int, c_int, c_int, c_int]),
         "nq_rank_for_bits": (c_int, [c_int, c_int, ctypes.c_double, c_int]),
         "nq_status_string": (ctypes.c_char_p, [c_int]),
@@ -176,6 +181,67 @@ def linear_into_profiled(x: torch.Tensor, layer: Layer, y: torch.Tensor, workspa
                                         workspace.data_ptr(), workspace.numel(), _stream(stream), PATHS[path],
                                         ctypes.cast(arr, ctypes.c_void_p), len(events), ctypes.byref(nl),
                                         ctypes.cast(dims, ctypes.c_void_p)))
+    k = min(nl.value, len(events) - 1)
+    return [(dims[2 * i], dims[2 * i + 1]) for i in range(k)]
+
+
+def _group_arrays(layers, ys=None):
+    refs = (ctypes.POINTER(nq_layer) * len(layers))(*[ctypes.pointer(L.c) for L in layers])
+    yp = None if ys is None else (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    return refs, yp
+
+
+def workspace_bytes_group(layers, B: int) -> int:
+    refs, _ = _group_arrays(layers)
+    return int(lib().nq_workspace_bytes_group(ctypes.cast(refs, ctypes.c_void_p), len(layers), B))
+
+
+def _check_group(x, layers, ys):
+    B = x.shape[0] if x.dim() == 2 else 1
+    if len(ys) != len(layers):
+        raise NQError(NQ_ERR_INVALID_ARG, "one output per layer")
+    if x.dtype not in (torch.bfloat16, torch.float32) or any(y.dtype != ys[0].dtype for y in ys) or \
+            ys[0].dtype not in (torch.bfloat16, torch.float32):
+        raise NQError(NQ_ERR_INVALID_ARG, "x and the outputs must be bf16 or fp32 (one dtype for all outputs)")
+    if not x.is_contiguous() or not all(y.is_contiguous() for y in ys):
+        raise NQError(NQ_ERR_INVALID_ARG, "x and the outputs must be contiguous")
+    if any(x.numel() != B * L.n for L in layers) or any(y.numel() != B * L.m for y, L in zip(ys, layers)):
+        raise NQError(NQ_ERR_INVALID_ARG, "x or an output has the wrong number of elements")
+    return B
+
+
+def linear_group_into(x: torch.Tensor, layers, ys, workspace: torch.Tensor, stream=None):
+    """ys[l] = x W_hat_l^T for layers sharing x (q/k/v, gate/up): two launches
+    in all for B <= 4 (stage 1 over every layer's V^T, block-diagonal stage 2)."""
+    B = _check_group(x, layers, ys)
+    refs, yp = _group_arrays(layers, ys)
+    _check(lib().nq_linear_fwd_group(ctypes.cast(refs, ctypes.c_void_p), len(layers), x.data_ptr(), _DT[x.dtype],
+                                     ctypes.cast(yp, ctypes.c_void_p), _DT[ys[0].dtype], B, workspace.data_ptr(),
+                                     workspace.numel(), _stream(stream)))
+    return ys
+
+
+def linear_group(x: torch.Tensor, layers, out_dtype: torch.dtype | None = None, stream=None):
+    xx = x if x.dim() == 2 else x.view(1, -1)
+    ys = [torch.empty((xx.shape[0], L.m), dtype=out_dtype or x.dtype, device=x.device) for L in layers]
+    ws = torch.empty(max(workspace_bytes_group(layers, xx.shape[0]), 256), dtype=torch.uint8, device=x.device)
+    linear_group_into(xx, layers, ys, ws, stream)
+    return ys if x.dim() == 2 else [y.view(-1) for y in ys]
+
+
+def linear_group_into_profiled(x: torch.Tensor, layers, ys, workspace: torch.Tensor, events, stream=None):
+    """linear_group_into that records HIP events around each launch; returns
+    [(workgroups, threads per workgroup)] of the launches."""
+    B = _check_group(x, layers, ys)
+    refs, yp = _group_arrays(layers, ys)
+    arr = (ctypes.c_void_p * len(events))(*events)
+    dims = (ctypes.c_int32 * (2 * len(events)))()
+    nl = ctypes.c_int32(0)
+    _check(lib().nq_linear_fwd_group_profiled(ctypes.cast(refs, ctypes.c_void_p), len(layers), x.data_ptr(),
+                                              _DT[x.dtype], ctypes.cast(yp, ctypes.c_void_p), _DT[ys[0].dtype], B,
+                                              workspace.data_ptr(), workspace.numel(), _stream(stream),
+                                              ctypes.cast(arr, ctypes.c_void_p), len(events), ctypes.byref(nl),
+                                              ctypes.cast(dims, ctypes.c_void_p)))
     k = min(nl.value, len(events) - 1)
     return [(dims[2 * i], dims[2 * i + 1]) for i in range(k)]
 

@@ -247,6 +247,130 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   return ok();
 }
 
+// ------------------------------------------------------------------ layer groups
+static_assert(NQ_GROUP_MAX == nq::GROUP_MAX, "one group size for the header and the kernels");
+static bool spans_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+static nq::GroupPlan group_plan_of(const nq_layer* const* layers, int32_t L, int32_t B) {
+  int m[NQ_GROUP_MAX], r[NQ_GROUP_MAX];
+  for (int l = 0; l < L; l++) {
+    m[l] = layers[l]->m;
+    r[l] = layers[l]->r;
+  }
+  return nq::group_plan(m, r, L, layers[0]->n, B);
+}
+
+static nq_status check_group(const nq_layer* const* layers, int32_t L) {
+  if (!layers) return fail(NQ_ERR_INVALID_ARG, "layers is NULL");
+  if (L < 1 || L > NQ_GROUP_MAX) return fail(NQ_ERR_INVALID_ARG, "group of %d layers (1..%d)", L, NQ_GROUP_MAX);
+  for (int l = 0; l < L; l++) {
+    nq_status st = check_layer(layers[l]);
+    if (st) return st;
+    if (layers[l]->n != layers[0]->n)
+      return fail(NQ_ERR_INVALID_ARG, "layer %d has n=%d, layer 0 has n=%d: a group shares x", l, layers[l]->n,
+                  layers[0]->n);
+    if (layers[l]->scale_dtype != layers[0]->scale_dtype)
+      return fail(NQ_ERR_INVALID_ARG, "layer %d has another scale dtype than layer 0", l);
+  }
+  return NQ_OK;
+}
+
+size_t nq_workspace_bytes_group(const nq_layer* const* layers, int32_t L, int32_t B) {
+  if (check_group(layers, L) || B <= 0 || B > MAX_BATCH) return 0;
+  const nq::GroupPlan p = group_plan_of(layers, L, B);
+  if (p.ok) return p.bytes;
+  size_t need = 0;  // one layer after another
+  for (int l = 0; l < L; l++) {
+    const size_t b = plan_bytes(layers[l], B, auto_path(layers[l], B));
+    need = b > need ? b : need;
+  }
+  return need;
+}
+
+static nq_status group_impl(const nq_layer* const* layers, int32_t L, const void* x, int32_t x_dtype,
+                            void* const* ys, int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
+                            nq_stream_t stream, nq::LaunchMarks* marks) {
+  nq_status st = check_group(layers, L);
+  if (st) return st;
+  if (B < 0 || B > MAX_BATCH) return fail(NQ_ERR_INVALID_ARG, "batch %d out of range 0..%d", B, MAX_BATCH);
+  const int xb = act_bytes(x_dtype), yb = act_bytes(y_dtype);
+  if (!xb) return fail(NQ_ERR_INVALID_ARG, "x_dtype %d is not NQ_BF16 or NQ_F32", x_dtype);
+  if (!yb) return fail(NQ_ERR_INVALID_ARG, "y_dtype %d is not NQ_BF16 or NQ_F32", y_dtype);
+  if (B == 0) return ok();
+  if (!x || !ys) return fail(NQ_ERR_INVALID_ARG, "x and ys must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(x) % xb) return fail(NQ_ERR_INVALID_ARG, "x is not aligned to its element size");
+  const size_t xn = (size_t)B * layers[0]->n * xb;
+  for (int l = 0; l < L; l++) {
+    if (!ys[l]) return fail(NQ_ERR_INVALID_ARG, "ys[%d] is NULL", l);
+    if (reinterpret_cast<uintptr_t>(ys[l]) % yb)
+      return fail(NQ_ERR_INVALID_ARG, "ys[%d] is not aligned to its element size", l);
+    const size_t yn = (size_t)B * layers[l]->m * yb;
+    if (spans_overlap(x, xn, ys[l], yn)) return fail(NQ_ERR_INVALID_ARG, "x and ys[%d] overlap", l);
+    for (int k = 0; k < l; k++)
+      if (spans_overlap(ys[k], (size_t)B * layers[k]->m * yb, ys[l], yn))
+        return fail(NQ_ERR_INVALID_ARG, "ys[%d] and ys[%d] overlap", k, l);
+  }
+  const nq::GroupPlan p = group_plan_of(layers, L, B);
+  const size_t need = nq_workspace_bytes_group(layers, L, B);
+  if (workspace_bytes < need)
+    return fail(NQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
+  if (need && !workspace) return fail(NQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(NQ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (!p.ok) {
+    if (marks) return fail(NQ_ERR_UNSUPPORTED, "timing marks need the fused group path (B <= 4)");
+    for (int l = 0; l < L; l++) {  // one layer after another, each on its automatic path
+      st = fwd_impl(layers[l], x, x_dtype, ys[l], y_dtype, B, workspace, workspace_bytes, stream, NQ_PATH_AUTO,
+                    nullptr);
+      if (st) return st;
+    }
+    return ok();
+  }
+  nq::GroupArgs a;
+  a.L = L;
+  a.n = layers[0]->n;
+  a.B = B;
+  for (int l = 0; l < L; l++) {
+    a.m[l] = layers[l]->m;
+    a.r[l] = layers[l]->r;
+    a.blob[l] = static_cast<const uint8_t*>(layers[l]->blob);
+    a.y[l] = ys[l];
+  }
+  a.scale_dtype = layers[0]->scale_dtype;
+  a.x_dtype = x_dtype;
+  a.y_dtype = y_dtype;
+  a.x = x;
+  a.ws = static_cast<uint8_t*>(workspace);
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  a.marks = marks;
+  (void)hipGetLastError();
+  const hipError_t e = nq::group_forward(a, p);
+  if (e != hipSuccess) return hip_fail(e, "group forward launch");
+  return ok();
+}
+
+nq_status nq_linear_fwd_group(const nq_layer* const* layers, int32_t L, const void* x, int32_t x_dtype,
+                              void* const* ys, int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
+                              nq_stream_t stream) {
+  return group_impl(layers, L, x, x_dtype, ys, y_dtype, B, workspace, workspace_bytes, stream, nullptr);
+}
+
+nq_status nq_linear_fwd_group_profiled(const nq_layer* const* layers, int32_t L, const void* x, int32_t x_dtype,
+                                       void* const* ys, int32_t y_dtype, int32_t B, void* workspace,
+                                       size_t workspace_bytes, nq_stream_t stream, void* const* events,
+                                       int32_t n_events, int32_t* n_launches, int32_t* launch_dims) {
+  if (!events || n_events < 1 || !n_launches) return fail(NQ_ERR_INVALID_ARG, "events and n_launches must be given");
+  nq::LaunchMarks marks;
+  marks.ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  marks.n = n_events;
+  marks.dims = launch_dims;
+  nq_status st = group_impl(layers, L, x, x_dtype, ys, y_dtype, B, workspace, workspace_bytes, stream, &marks);
+  *n_launches = marks.k > 0 ? marks.k - 1 : 0;
+  return st;
+}
+
 nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
                              void* workspace, size_t workspace_bytes, nq_stream_t stream, int32_t path) {
   return fwd_impl(L, x, x_dtype, y, y_dtype, B, workspace, workspace_bytes, stream, path, nullptr);

@@ -23,6 +23,8 @@
 // Every load of a prologue is issued before the weights and without a branch,
 // so a prologue costs one memory round trip and the encoder never waits for
 // the weight stream.
+#include <climits>
+
 #include "nq_common.h"
 #include "nq_internal.h"
 
@@ -37,8 +39,9 @@ namespace {
 constexpr int P = 4;                    // e4m3 pieces per value
 constexpr int DEC_MAX_B = 4;           // batch rows of the decode path (4 pieces x B <= 16 MFMA columns)
 constexpr int TARGET_WG = 256;          // one workgroup per CU of an MI355X
-constexpr int MIN_WG = 128;
-constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles             // fewest workgroups a stage is cut into (half the CUs)
+constexpr int MIN_WG = 128;             // fewest workgroups a stage is cut into (half the CUs)
+constexpr int WAVE_BUDGET = 256 * 12;   // resident waves of the chip at <= 168 VGPRs (3 per SIMD)
+constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles
 constexpr size_t LDS_S1 = 64 * 1024;    // image bytes a stage-1 workgroup may stage
 constexpr size_t LDS_S2 = 64 * 1024;    // image (+ reduction) bytes of a stage-2 workgroup
 
@@ -565,19 +568,19 @@ struct S1Args {
   int red_off;         // byte offset of the reduction buffer in LDS
 };
 
+// The work of one stage-1 workgroup: row group `rowgroup` (RM row tiles) of
+// column split `split`.
 template <typename XT, typename ST, int BB, int RM>
-__global__ void __launch_bounds__(512) dec_s1_kernel(S1Args a) {
+__device__ __forceinline__ void s1_body(const S1Args& a, int rowgroup, int split, uint8_t* lds) {
   constexpr int CW = 4 * BB;
-  extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.y;
   const int kt0 = split * a.KL;
   const int kt1 = min(a.KT, kt0 + a.KL);
   const int KLr = kt1 - kt0;
   const int q0 = kt0 >> 2, q1 = (kt1 + 3) >> 2;
   WaveWork<RM> ww;
-  ww.rt0 = blockIdx.x * RM;
+  ww.rt0 = rowgroup * RM;
   const int RG = min(RM, a.RT - ww.rt0);
   ww.qa = q0 + (int)(((long long)(q1 - q0) * wave) / a.KS);
   ww.qb = q0 + (int)(((long long)(q1 - q0) * (wave + 1)) / a.KS);
@@ -615,6 +618,31 @@ __global__ void __launch_bounds__(512) dec_s1_kernel(S1Args a) {
   });
 }
 
+template <typename XT, typename ST, int BB, int RM>
+__global__ void __launch_bounds__(512) dec_s1_kernel(S1Args a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  s1_body<XT, ST, BB, RM>(a, blockIdx.x, blockIdx.y, lds);
+}
+
+// Stage 1 of up to MAX_GROUP layers that share x, in one launch: workgroup
+// blockIdx.x belongs to the layer whose range of row groups holds it.
+constexpr int MAX_GROUP = GROUP_MAX;
+struct S1Group {
+  S1Args l[MAX_GROUP];
+  int wg_end[MAX_GROUP];  // cumulative row groups (unused entries: INT_MAX)
+};
+
+template <typename XT, typename ST, int BB, int RM>
+__global__ void __launch_bounds__(512) dec_s1_group_kernel(S1Group g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int bx = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_GROUP - 1; i++) l += bx >= g.wg_end[i] ? 1 : 0;
+  const int begin = l == 0 ? 0 : g.wg_end[l - 1];
+  s1_body<XT, ST, BB, RM>(g.l[l], bx - begin, blockIdx.y, lds);
+}
+
 // ------------------------------------------------------------------ stage 2
 // Workgroup = row group of RG row tiles; its KS waves split the quads of the
 // rank dimension.  Prologue: t' = g * (sum of partials) encoded into LDS (or a
@@ -635,15 +663,15 @@ struct S2Args {
   int s1_off;  // byte offset of the staged output scales in LDS
 };
 
+// The work of one stage-2 workgroup: row group `rowgroup` (RM row tiles).
 template <typename ST, bool FUSED, int BB, int RM, int SM>
-__global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
+__device__ __forceinline__ void s2_body(const S2Args& a, int rowgroup, uint8_t* lds) {
   constexpr int CW = 4 * BB;
-  extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nq = (a.KT + 3) >> 2;
   WaveWork<RM> ww;
-  ww.rt0 = blockIdx.x * RM;
+  ww.rt0 = rowgroup * RM;
   const int RG = min(RM, a.RT - ww.rt0);
   ww.qa = (int)(((long long)nq * wave) / a.KS);
   ww.qb = (int)(((long long)nq * (wave + 1)) / a.KS);
@@ -709,6 +737,29 @@ __global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
   });
 }
 
+template <typename ST, bool FUSED, int BB, int RM, int SM>
+__global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  s2_body<ST, FUSED, BB, RM, SM>(a, blockIdx.x, lds);
+}
+
+// Stage 2 of a group of layers (block-diagonal: each layer its own U, t and y).
+struct S2Group {
+  S2Args l[MAX_GROUP];
+  int wg_end[MAX_GROUP];
+};
+
+template <typename ST, int BB, int RM, int SM>
+__global__ void __launch_bounds__(512) dec_s2_group_kernel(S2Group g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int bx = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_GROUP - 1; i++) l += bx >= g.wg_end[i] ? 1 : 0;
+  const int begin = l == 0 ? 0 : g.wg_end[l - 1];
+  s2_body<ST, true, BB, RM, SM>(g.l[l], bx - begin, lds);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ plan
@@ -718,15 +769,14 @@ __global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
 // (every workgroup encodes its own copy of its activation range, so fewer,
 // taller workgroups encode less) and whose 16-quad buffer holds RM x
 // ceil(quads/KS); KS as large as the quads allow (the prologue's parallelism)
-// while the whole grid stays within 8 resident waves per CU, so that it runs
-// in one round.  False if no shape fits.
+// while the whole grid stays within WAVE_BUDGET resident waves, so that it
+// runs in one round.  False if no shape fits.
 static bool pick_shape(int RT, int splits, int quads, int minwg, int* RM, int* KS) {
   for (int rm = 8; rm >= 1; rm /= 2) {
     const int wgs = ceil_div(RT, rm) * splits;
     if (rm > 1 && wgs < minwg) continue;
     int ks = quads < 8 ? quads : 8;
-    const int per_cu = ceil_div(wgs, TARGET_WG);  // workgroups a CU must hold at once
-    while (ks > 1 && per_cu * ks > 8) ks--;
+    while (ks > 1 && wgs * ks > WAVE_BUDGET) ks--;
     const int qw = ceil_div(quads, ks);
     if (rm * qw > 16) continue;
     *RM = rm;
@@ -819,6 +869,16 @@ static void launch_s2(int RG, dim3 g, dim3 b, size_t lds, hipStream_t st, const 
   }
 }
 
+template <typename ST, int BB, int SM>
+static void launch_s2_group(int RG, dim3 g, dim3 b, size_t lds, hipStream_t st, const S2Group& k) {
+  switch (RG) {
+    case 8: hipLaunchKernelGGL((dec_s2_group_kernel<ST, BB, 8, SM>), g, b, lds, st, k); break;
+    case 4: hipLaunchKernelGGL((dec_s2_group_kernel<ST, BB, 4, SM>), g, b, lds, st, k); break;
+    case 2: hipLaunchKernelGGL((dec_s2_group_kernel<ST, BB, 2, SM>), g, b, lds, st, k); break;
+    default: hipLaunchKernelGGL((dec_s2_group_kernel<ST, BB, 1, SM>), g, b, lds, st, k); break;
+  }
+}
+
 template <typename XT, typename ST, int BB>
 static hipError_t dec_forward_t(const FwdArgs& a, const DecPlan& p) {
   const int sb = sizeof(ST);
@@ -885,6 +945,159 @@ static hipError_t dec_forward_b(const FwdArgs& a, const DecPlan& p) {
     case 3: return dec_forward_t<XT, ST, 3>(a, p);
     default: return dec_forward_t<XT, ST, 4>(a, p);
   }
+}
+
+GroupPlan group_plan(const int* m, const int* r, int L, int n, int B) {
+  GroupPlan p{};
+  p.ok = false;
+  if (L < 1 || L > GROUP_MAX || B < 1 || B > DEC_MAX_B) return p;
+  p.L = L;
+  p.B = B;
+  p.CW = B * P;
+  const size_t tb = img_tile_bytes(p.CW, B);
+  const size_t red_bytes = (size_t)8 * 8 * 16 * 16;
+  p.KT1 = ceil_div(n, 128);
+  int rt1_sum = 0, rt2_sum = 0, rmax = 0, kt2max = 0;
+  for (int l = 0; l < L; l++) {
+    p.RT1[l] = ceil_div(r[l], 16);
+    p.Rpad1[l] = p.RT1[l] * 16;
+    p.RT2[l] = ceil_div(m[l], 16);
+    p.KT2[l] = ceil_div(r[l], 128);
+    rt1_sum += p.RT1[l];
+    rt2_sum += p.RT2[l];
+    rmax = r[l] > rmax ? r[l] : rmax;
+    kt2max = p.KT2[l] > kt2max ? p.KT2[l] : kt2max;
+  }
+  // stage 1: the rules of the single-layer plan, on the layers' rows together
+  const int quads1 = ceil_div(p.KT1, 4);
+  const int klmax = (int)((LDS_S1 - red_bytes) / tb) / 4 * 4;
+  if (klmax < 4) return p;
+  {
+    int rm, ks;
+    if (!pick_shape(rt1_sum, 1, 4, MIN_WG, &rm, &ks)) return p;
+    const int rowgroups = ceil_div(rt1_sum, rm);
+    const int smax = rmax >= 2048 ? 2 : 4;
+    int s = ceil_div(TARGET_WG, rowgroups);
+    s = s > smax ? smax : s;
+    s = s > quads1 ? quads1 : s;
+    s = s < 1 ? 1 : s;
+    const int s_lds = ceil_div(p.KT1, klmax);
+    if (s < s_lds) s = s_lds;
+    if (s == 3) s = 4;
+    p.KL1 = 4 * ceil_div(ceil_div(p.KT1, s), 4);
+    p.S1 = ceil_div(p.KT1, p.KL1);
+    if (!pick_shape(rt1_sum, p.S1, ceil_div(p.KL1, 4), MIN_WG, &p.RG1, &p.KS1)) return p;
+  }
+  if (p.S1 * B > 4 || p.S1 == 3) return p;  // stage 2 folds the partial sums in its prologue
+  p.red1 = align_up((size_t)p.KL1 * tb, 16);
+  p.lds1 = p.red1 + red_bytes;
+  // stage 2: one shape for all layers, sized for the longest rank
+  const int quads2 = ceil_div(kt2max, 4);
+  if (!pick_shape(rt2_sum, 1, quads2, MIN_WG, &p.RG2, &p.KS2)) return p;
+  {
+    const int chunks = B * kt2max * 16;
+    int rm, ks;
+    if (chunks > 2 * 64 * p.KS2 && pick_shape(rt2_sum, 1, quads2, MIN_WG * 3 / 4, &rm, &ks) &&
+        chunks <= 2 * 64 * ks) {
+      p.RG2 = rm;
+      p.KS2 = ks;
+    }
+  }
+  p.red2 = align_up((size_t)kt2max * tb, 16);
+  p.lds2 = p.red2 + red_bytes + S1_LDS_BYTES;
+  if (p.lds2 > LDS_S2) return p;
+  int e1 = 0, e2 = 0;
+  for (int l = 0; l < GROUP_MAX; l++) {
+    if (l < L) {
+      e1 += ceil_div(p.RT1[l], p.RG1);
+      e2 += ceil_div(p.RT2[l], p.RG2);
+      p.wg1_end[l] = e1;
+      p.wg2_end[l] = e2;
+    } else {
+      p.wg1_end[l] = INT_MAX;
+      p.wg2_end[l] = INT_MAX;
+    }
+  }
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  for (int l = 0; l < L; l++) p.off_part[l] = take((size_t)p.S1 * B * p.Rpad1[l] * 4);
+  p.off_xpad = take((size_t)B * align_up(n, 8) * 4);
+  p.bytes = o;
+  p.ok = true;
+  return p;
+}
+
+template <typename XT, typename ST, int BB>
+static hipError_t group_forward_t(const GroupArgs& a, const GroupPlan& p) {
+  hipStream_t st = a.stream;
+  FwdArgs fa{};  // for the timing marks only
+  fa.stream = st;
+  fa.marks = a.marks;
+  const bool xvec = (a.n % 8 == 0) && (reinterpret_cast<uintptr_t>(a.x) % 16 == 0);
+  const void* x = a.x;
+  int xstride = a.n;
+  if (!xvec) {
+    xstride = align_up(a.n, 8);
+    XT* xp = reinterpret_cast<XT*>(a.ws + p.off_xpad);
+    const int tot = a.B * xstride;
+    mark(fa, dim3(ceil_div(tot, 256)), dim3(256));
+    hipLaunchKernelGGL((dec_xpad_kernel<XT>), dim3(ceil_div(tot, 256)), dim3(256), 0, st,
+                       reinterpret_cast<const XT*>(a.x), a.n, a.B, xstride, xp);
+    x = xp;
+  }
+  S1Group g1{};
+  S2Group g2{};
+  const int sb = sizeof(ST);
+  for (int l = 0; l < MAX_GROUP; l++) {
+    g1.wg_end[l] = p.wg1_end[l];
+    g2.wg_end[l] = p.wg2_end[l];
+    if (l >= a.L) continue;
+    const BlobLayout L = blob_layout(a.m[l], a.n, a.r[l], sb);
+    const uint8_t* blob = a.blob[l];
+    float* part = reinterpret_cast<float*>(a.ws + p.off_part[l]);
+    g1.l[l] = S1Args{reinterpret_cast<const uint32_t*>(blob + L.off_vt), p.RT1[l], p.KT1, p.KL1, p.RG1, p.KS1, x,
+                     blob + L.off_s2, a.n, xstride, p.CW, a.B, part, p.Rpad1[l], (int)p.red1};
+    g2.l[l] = S2Args{reinterpret_cast<const uint32_t*>(blob + L.off_u), p.RT2[l], p.KT2[l], p.RG2, p.KS2, nullptr,
+                     part, p.S1, p.Rpad1[l], a.r[l], blob + L.off_g, p.CW, a.B, blob + L.off_s1, a.scale_dtype,
+                     a.y[l], a.y_dtype == 0 ? 0 : 2, a.m[l], (int)p.red2, (int)(p.lds2 - S1_LDS_BYTES)};
+  }
+  const dim3 grid1(p.wg1_end[a.L - 1], p.S1), b1(64 * p.KS1);
+  mark(fa, grid1, b1);
+  switch (p.RG1) {
+    case 8: hipLaunchKernelGGL((dec_s1_group_kernel<XT, ST, BB, 8>), grid1, b1, p.lds1, st, g1); break;
+    case 4: hipLaunchKernelGGL((dec_s1_group_kernel<XT, ST, BB, 4>), grid1, b1, p.lds1, st, g1); break;
+    case 2: hipLaunchKernelGGL((dec_s1_group_kernel<XT, ST, BB, 2>), grid1, b1, p.lds1, st, g1); break;
+    default: hipLaunchKernelGGL((dec_s1_group_kernel<XT, ST, BB, 1>), grid1, b1, p.lds1, st, g1); break;
+  }
+  const dim3 grid2(p.wg2_end[a.L - 1]), b2(64 * p.KS2);
+  mark(fa, grid2, b2);
+  // splits folded by the prologue: 1, 2 or 4 (S1 * B <= 4)
+  if (p.S1 == 1) launch_s2_group<ST, BB, 1>(p.RG2, grid2, b2, p.lds2, st, g2);
+  else if (p.S1 == 2) launch_s2_group<ST, BB, (BB <= 2 ? 2 : 1)>(p.RG2, grid2, b2, p.lds2, st, g2);
+  else launch_s2_group<ST, BB, (BB == 1 ? 4 : 1)>(p.RG2, grid2, b2, p.lds2, st, g2);
+  mark(fa);
+  return hipGetLastError();
+}
+
+template <typename XT, typename ST>
+static hipError_t group_forward_b(const GroupArgs& a, const GroupPlan& p) {
+  switch (a.B) {
+    case 1: return group_forward_t<XT, ST, 1>(a, p);
+    case 2: return group_forward_t<XT, ST, 2>(a, p);
+    case 3: return group_forward_t<XT, ST, 3>(a, p);
+    default: return group_forward_t<XT, ST, 4>(a, p);
+  }
+}
+
+hipError_t group_forward(const GroupArgs& a, const GroupPlan& p) {
+  if (a.x_dtype == 2) {
+    return a.scale_dtype == 1 ? group_forward_b<uint16_t, _Float16>(a, p) : group_forward_b<uint16_t, float>(a, p);
+  }
+  return a.scale_dtype == 1 ? group_forward_b<float, _Float16>(a, p) : group_forward_b<float, float>(a, p);
 }
 
 hipError_t dec_forward(const FwdArgs& a, const DecPlan& p) {

@@ -86,6 +86,35 @@ struct DecPlan {
 DecPlan dec_plan(int m, int n, int r, int B);
 hipError_t dec_forward(const FwdArgs& a, const DecPlan& p);
 
+// Several layers that share x (same n, scale dtype, batch <= 4) in two
+// launches: stage 1 over all their V^T row tiles, stage 2 block-diagonal.
+constexpr int GROUP_MAX = 4;
+struct GroupPlan {
+  bool ok;
+  int L, B, CW;
+  int KT1, KL1, S1, RG1, KS1;   // stage 1, common to the layers
+  int RG2, KS2;                 // stage 2, common to the layers
+  int RT1[GROUP_MAX], Rpad1[GROUP_MAX], RT2[GROUP_MAX], KT2[GROUP_MAX];
+  int wg1_end[GROUP_MAX], wg2_end[GROUP_MAX];  // cumulative workgroups per layer
+  size_t lds1, lds2, red1, red2;
+  size_t off_part[GROUP_MAX], off_xpad;
+  size_t bytes;
+};
+GroupPlan group_plan(const int* m, const int* r, int L, int n, int B);
+
+struct GroupArgs {
+  int L, n, B;
+  int m[GROUP_MAX], r[GROUP_MAX];
+  int scale_dtype, x_dtype, y_dtype;
+  const uint8_t* blob[GROUP_MAX];
+  const void* x;
+  void* y[GROUP_MAX];
+  uint8_t* ws;
+  hipStream_t stream;
+  LaunchMarks* marks = nullptr;
+};
+hipError_t group_forward(const GroupArgs& a, const GroupPlan& p);
+
 struct ValuPlan {
   StagePlan s1, s2;
   size_t off_v1, off_part1, off_v2, off_part2, off_sums;

@@ -127,6 +127,29 @@ nq_status nq_linear_fwd_path(const nq_layer* L, const void* x, int32_t x_dtype, 
                              int32_t y_dtype, int32_t B, void* workspace, size_t workspace_bytes,
                              nq_stream_t stream, int32_t path);
 
+/* Layer groups (the fused block decode).  In a transformer block several
+ * linears read the same input: q, k and v, and gate and up (the 70B decode
+ * measured on the hardwired.dev NanoQuant page, section "Cisla").  A group of
+ * 1..NQ_GROUP_MAX layers with the same n and scale dtype is run on one x:
+ * ys[l] = x W_hat_l^T for each l, B x m_l row-major, y_dtype.  For B <= 4 it
+ * takes two launches in all: stage 1 over the V^T row tiles of every layer,
+ * then a block-diagonal stage 2 (each layer its own U, t and y); larger B
+ * runs the layers one after another on their automatic paths.  x must not
+ * overlap any ys[l], nor the ys each other; NQ_ERR_INVALID_ARG for a group
+ * whose layers differ in n or scale dtype.  Asynchronous like nq_linear_fwd. */
+#define NQ_GROUP_MAX 4
+size_t nq_workspace_bytes_group(const nq_layer* const* layers, int32_t L, int32_t B);
+nq_status nq_linear_fwd_group(const nq_layer* const* layers, int32_t L, const void* x, int32_t x_dtype,
+                              void* const* ys, int32_t y_dtype, int32_t B, void* workspace,
+                              size_t workspace_bytes, nq_stream_t stream);
+/* nq_linear_fwd_group with the timing marks of nq_linear_fwd_profiled (fused
+ * path only, NQ_ERR_UNSUPPORTED otherwise). */
+nq_status nq_linear_fwd_group_profiled(const nq_layer* const* layers, int32_t L, const void* x,
+                                       int32_t x_dtype, void* const* ys, int32_t y_dtype, int32_t B,
+                                       void* workspace, size_t workspace_bytes, nq_stream_t stream,
+                                       void* const* events, int32_t n_events, int32_t* n_launches,
+                                       int32_t* launch_dims);
+
 /* Bytes of the static device scratch used by nq_linear_fwd_noalloc. */
 #define NQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 

@@ -172,3 +172,41 @@ def test_status_strings(L):
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert L.nq_status_string(s)
     assert L.nq_status_string(42) == b"unknown status"
+
+
+# ------------------------------------------------------------------ layer groups
+def _group(layers):
+    return ctypes.cast((ctypes.POINTER(nq.nq_layer) * len(layers))(*[ctypes.pointer(l) for l in layers]),
+                       ctypes.c_void_p)
+
+
+def _ptrs(vals):
+    return ctypes.cast((ctypes.c_void_p * len(vals))(*vals), ctypes.c_void_p)
+
+
+def test_group_validation(L):
+    q, k = _layer(m=8192, n=8192, r=3257), _layer(m=1024, n=8192, r=710)
+    other_n = _layer(m=1024, n=4096, r=710)
+    ys = _ptrs([FAKE + (1 << 30), FAKE + (2 << 30)])
+    ws = L.nq_workspace_bytes_group(_group([q, k]), 2, 1)
+    assert ws > 0
+    run = lambda grp, n, yp, B=1, wsb=ws: L.nq_linear_fwd_group(grp, n, FAKE, nq.NQ_BF16, yp, nq.NQ_BF16, B, FAKE,
+                                                                wsb, None)
+    assert run(_group([q, k]), 0, ys) == nq.NQ_ERR_INVALID_ARG
+    assert run(_group([q, k]), nq.NQ_GROUP_MAX + 1, ys) == nq.NQ_ERR_INVALID_ARG
+    assert run(_group([q, other_n]), 2, ys) == nq.NQ_ERR_INVALID_ARG
+    assert b"shares x" in L.nq_last_error()
+    assert run(_group([q, k]), 2, _ptrs([FAKE + (1 << 30), FAKE + (1 << 30) + 64])) == nq.NQ_ERR_INVALID_ARG
+    assert b"overlap" in L.nq_last_error()
+    assert run(_group([q, k]), 2, _ptrs([FAKE, FAKE + (2 << 30)])) == nq.NQ_ERR_INVALID_ARG  # ys[0] on x
+    assert run(_group([q, k]), 2, ys, wsb=ws - 1) == nq.NQ_ERR_WORKSPACE
+    assert run(_group([q, k]), 2, ys, B=0) == nq.NQ_OK
+    assert L.nq_workspace_bytes_group(_group([q, other_n]), 2, 1) == 0
+
+
+def test_group_workspace_covers_the_fallback(L):
+    q, k = _layer(m=8192, n=8192, r=3257), _layer(m=1024, n=8192, r=710)
+    for B in (5, 16, 17, 2048):  # beyond the fused path: the layers run one after another
+        need = max(L.nq_workspace_bytes_path(ctypes.byref(l), B, 0) for l in (q, k))
+        assert L.nq_workspace_bytes_group(_group([q, k]), 2, B) <= need
+        assert L.nq_workspace_bytes_group(_group([q, k]), 2, B) > 0
