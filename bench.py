@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemv", "valu"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="time the 560 linears one by one (no layer groups)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill section")
     ap.add_argument("--suite", default=None, choices=["7b"])
     ap.add_argument("--out", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -341,6 +342,71 @@ def time_graph(torch, stream, step, warmup, steps):
     return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
 
+MFMA_PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+
+
+def run_prefill70b(dev, tokens=2048, bpw=0.8, reps=5):
+    """One 70B block's distinct linear shapes at `tokens` rows (the prefill
+    path: fp16 MFMA GEMMs with exact +-1 operands), each timed per kernel with
+    HIP events on its stream; MFMA utilisation = 2 B r (m + n) / (t x peak).
+    Eight sampled output rows per shape are checked against the fp64 oracle."""
+    import numpy as np
+    import torch
+    import binary_rank_gemv_packed_amd as nq
+    import synth
+    from oracle import nq_oracle as O
+    hip = hip_runtime()
+    stream = torch.cuda.Stream()
+    out, block_s, block_flops = {}, 0.0, 0.0
+    for name in ("q", "k", "gate", "down"):
+        m, n = synth.LLAMA70B[name]
+        r = nq.rank_for_bits(m, n, bpw, 16)
+        layer, x, host = make_layer_gpu(m, n, r, tokens, 777 + m + 3 * n, dev, keep=True)
+        y = torch.empty(tokens, m, device=dev, dtype=torch.bfloat16)
+        ws = torch.empty(nq.workspace_bytes(layer, tokens, "gemm"), dtype=torch.uint8, device=dev)
+        ev = Events(hip, 8 * reps)
+        with torch.cuda.stream(stream):
+            nq.linear_into(x, layer, y, ws, "gemm")
+            launches = []
+            for k in range(reps):
+                launches = nq.linear_into_profiled(x, layer, y, ws, ev.ev[8 * k:8 * k + 8], "gemm")
+        torch.cuda.synchronize()
+        nk = len(launches)
+        per = [statistics.mean(ev.ms(8 * k + j, 8 * k + j + 1) for k in range(reps)) for j in range(nk)]
+        total = statistics.mean(ev.ms(8 * k, 8 * k + nk) for k in range(reps))
+        ev.close()
+        flops = 2.0 * tokens * r * (m + n)
+        f1, f2 = 2.0 * tokens * r * n, 2.0 * tokens * r * m
+        rows = np.linspace(0, tokens - 1, 8).astype(int)
+        yy = y[rows].float().cpu().numpy()
+        f64 = lambda a: np.asarray(a, np.float64)
+        ref = O.linear_factored(f64(host["x"][rows]), host["U"], host["V"], f64(host["s1"]), f64(host["g"]),
+                                f64(host["s2"]))
+        rr = synth.round_to_bf16(ref.astype(np.float32)).astype(np.float64)
+        e = float(np.linalg.norm(yy - ref) / np.linalg.norm(ref))
+        er = float(np.linalg.norm(rr - ref) / np.linalg.norm(ref))
+        out[name] = {"m": m, "n": n, "r": r, "ms": round(total, 4), "tflops": round(flops / (total * 1e-3) / 1e12, 1),
+                     "mfma_util": round(flops / (total * 1e-3) / 1e12 / MFMA_PEAK_FP16_TFLOPS, 4),
+                     "gemm_xv_ms": round(per[1], 4), "gemm_xv_util": round(f1 / (per[1] * 1e-3) / 1e12 /
+                                                                           MFMA_PEAK_FP16_TFLOPS, 4),
+                     "gemm_tu_ms": round(per[3], 4), "gemm_tu_util": round(f2 / (per[3] * 1e-3) / 1e12 /
+                                                                           MFMA_PEAK_FP16_TFLOPS, 4),
+                     "sampled_rows_rel_l2": float(f"{e:.3e}"), "bf16_rounding_rel_l2": float(f"{er:.3e}"),
+                     "ok": bool(e <= 2e-3 + er)}
+        c = {"q": 2, "k": 2, "gate": 2, "down": 1}[name]  # q~o, k~v, gate~up
+        block_s += c * total * 1e-3
+        block_flops += c * flops
+        log(f"[bench] prefill {name}: {total:.3f} ms, {out[name]['tflops']} TFLOP/s, "
+            f"MFMA util {out[name]['mfma_util']:.3f}, sampled rows rel L2 {e:.2e}")
+        del layer, x, y, ws, host
+        torch.cuda.empty_cache()
+    return {"workload": f"llama2-70b block linears at {tokens} tokens, {bpw} bpw, bf16 x and y, fp16 scales",
+            "per_shape": out, "block_ms": round(block_s * 1e3, 3),
+            "block_tflops": round(block_flops / block_s / 1e12, 1),
+            "mfma_util": round(block_flops / block_s / 1e12 / MFMA_PEAK_FP16_TFLOPS, 4),
+            "peak_tflops": MFMA_PEAK_FP16_TFLOPS, "tokens_per_s": round(tokens / (block_s * 80), 1)}
+
+
 def run_decode70b(args):
     import torch
     import binary_rank_gemv_packed_amd as nq
@@ -459,6 +525,10 @@ def run_decode70b(args):
                                 "speedup_of_fused": round(unfused_ms / ms, 3)}
     if roof is not None:
         out["roofline"] = roof
+    if not args.no_prefill:
+        del layers, xs, ys, ws
+        torch.cuda.empty_cache()
+        out["prefill"] = run_prefill70b(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline(spec, B)
