@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         "nq_layer_bytes": (c_size, [c_int, c_int, c_int, c_int]),
         "nq_pack_factors": (c_int, [P, vp, vp, vp, vp, vp, vp]),
         "nq_unpack_factors": (c_int, [P, vp, vp, vp]),
+        "nq_transpose_layer": (c_int, [P, P, vp]),
         "nq_workspace_bytes": (c_size, [P, c_int]),
         "nq_workspace_bytes_path": (c_size, [P, c_int, c_int]),
         "nq_linear_fwd": (c_int, [P, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
@@ -142,6 +143,14 @@ def unpack(layer: Layer, stream=None):
     V = torch.empty((layer.n, layer.r), dtype=torch.int8, device=layer.device)
     _check(lib().nq_unpack_factors(layer.ref, U.data_ptr(), V.data_ptr(), _stream(stream)))
     return U, V
+
+
+def transpose(layer: Layer, stream=None) -> Layer:
+    """The layer of W_hat^T (U and V, s1 and s2 swapped, factors bit-transposed
+    on the GPU): linear(dy, transpose(layer)) = dy W_hat, the backward product."""
+    out = empty_layer(layer.n, layer.m, layer.r, layer.scale_dtype, device=layer.device)
+    _check(lib().nq_transpose_layer(layer.ref, out.ref, _stream(stream)))
+    return out
 
 
 def workspace_bytes(layer: Layer, B: int, path: str = "auto") -> int:

@@ -130,6 +130,59 @@ nq_status nq_pack_factors(const nq_layer* L, const int8_t* U, const int8_t* V, c
   return ok();
 }
 
+nq_status nq_transpose_layer(const nq_layer* src, const nq_layer* dst, nq_stream_t stream) {
+  nq_status st = check_layer(src);
+  if (st) return st;
+  st = check_layer(dst);
+  if (st) return st;
+  if (dst->m != src->n || dst->n != src->m || dst->r != src->r)
+    return fail(NQ_ERR_INVALID_ARG, "dst must be %d x %d of rank %d (the transpose of src), got %d x %d rank %d",
+                src->n, src->m, src->r, dst->m, dst->n, dst->r);
+  if (dst->scale_dtype != src->scale_dtype) return fail(NQ_ERR_INVALID_ARG, "dst and src differ in scale dtype");
+  const int sb = scale_bytes(src->scale_dtype);
+  const nq::BlobLayout S = nq::blob_layout(src->m, src->n, src->r, sb);
+  const nq::BlobLayout D = nq::blob_layout(dst->m, dst->n, dst->r, sb);
+  {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src->blob), d0 = reinterpret_cast<uintptr_t>(dst->blob);
+    if (s0 < d0 + D.total && d0 < s0 + S.total) return fail(NQ_ERR_INVALID_ARG, "src and dst blobs overlap");
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* in = static_cast<const uint8_t*>(src->blob);
+  uint8_t* out = static_cast<uint8_t*>(dst->blob);
+  nq::BlobHeader h;
+  memset(&h, 0, sizeof(h));
+  h.magic = nq::BLOB_MAGIC;
+  h.version = nq::BLOB_VERSION;
+  h.m = dst->m;
+  h.n = dst->n;
+  h.r = dst->r;
+  h.scale_dtype = dst->scale_dtype;
+  h.off_u = D.off_u;
+  h.off_vt = D.off_vt;
+  h.off_s1 = D.off_s1;
+  h.off_g = D.off_g;
+  h.off_s2 = D.off_s2;
+  h.total = D.total;
+  (void)hipGetLastError();
+  hipError_t e = hipMemcpyAsync(out, &h, sizeof(h), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "header copy");
+  // s1' = s2 (m' = n outputs), g' = g, s2' = s1 (n' = m inputs)
+  e = hipMemcpyAsync(out + D.off_s1, in + S.off_s2, (size_t)src->n * sb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(out + D.off_g, in + S.off_g, (size_t)src->r * sb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(out + D.off_s2, in + S.off_s1, (size_t)src->m * sb, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "scale copy");
+  // U' = V (n x r) is the transpose of the stored V^T (r x n); V'^T = U^T (r x m) that of U (m x r)
+  e = nq::launch_transpose(reinterpret_cast<const uint32_t*>(in + S.off_vt), src->r, src->n,
+                           reinterpret_cast<uint32_t*>(out + D.off_u), s);
+  if (e == hipSuccess)
+    e = nq::launch_transpose(reinterpret_cast<const uint32_t*>(in + S.off_u), src->m, src->r,
+                             reinterpret_cast<uint32_t*>(out + D.off_vt), s);
+  if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "transpose synchronise");
+  return ok();
+}
+
 nq_status nq_unpack_factors(const nq_layer* L, int8_t* U, int8_t* V, nq_stream_t stream) {
   nq_status st = check_layer(L);
   if (st) return st;

@@ -9,6 +9,7 @@ namespace nq {
 
 hipError_t launch_pack(const int8_t* M, int R, int C, long long ld_row, long long ld_col, uint32_t* out,
                        int* bad_count, hipStream_t s);
+hipError_t launch_transpose(const uint32_t* src, int R, int C, uint32_t* dst, hipStream_t s);
 hipError_t launch_unpack(const uint32_t* in, int R, int C, long long ld_row, long long ld_col, int8_t* M,
                          hipStream_t s);
 

@@ -58,6 +58,46 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint32_t* __restrict_
   }
 }
 
+// Transpose of a packed sign matrix: src is R x C, dst (C x R) gets
+// dst(i, c) = src(c, i).  One thread per dst word; its 32 bits come from 32
+// consecutive src rows at one src column, i.e. one fixed bit position of 32
+// src words (two row tiles' lanes), which neighbouring threads share through
+// the caches.  Padding bits of dst are zero, as pack_kernel writes them.
+__global__ void __launch_bounds__(256) transpose_kernel(const uint32_t* __restrict__ src, int R, int C, int KTs,
+                                                        uint32_t* __restrict__ dst, int RTd, int KTd) {
+  long long wid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  long long total = (long long)RTd * KTd * TILE_WORDS;
+  if (wid >= total) return;
+  const int lane = (int)(wid % TILE_WORDS);
+  const long long t = wid / TILE_WORDS;
+  const int kt = (int)(t % KTd);
+  const int rt = (int)(t / KTd);
+  const int c = rt * TILE_ROWS + (lane & 15);  // dst row = src column
+  uint32_t word = 0;
+  if (c < C) {
+    const int ktc = c / TILE_COLS, cc = c % TILE_COLS;
+    const int sgrp = cc >> 5, c32 = cc & 31;
+    const int sbit = 4 * (c32 & 7) + (c32 >> 3);  // bit of column c32 in a word: packed_bit_col inverted
+    for (int b = 0; b < 32; b++) {
+      const int sr = kt * TILE_COLS + packed_bit_col(lane, b);  // dst column = src row
+      if (sr < R) {
+        const int slane = (sr & 15) + 16 * sgrp;
+        const uint32_t w = src[packed_word_index(sr / TILE_ROWS, ktc, slane, KTs)];
+        word |= ((w >> sbit) & 1u) << b;
+      }
+    }
+  }
+  dst[packed_word_index(rt, kt, lane, KTd)] = word;
+}
+
+hipError_t launch_transpose(const uint32_t* src, int R, int C, uint32_t* dst, hipStream_t s) {
+  const PackedDims ds = packed_dims(R, C), dd = packed_dims(C, R);
+  const long long total = (long long)dd.RT * dd.KT * TILE_WORDS;
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(transpose_kernel, dim3(blocks), dim3(256), 0, s, src, R, C, ds.KT, dst, dd.RT, dd.KT);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const int8_t* M, int R, int C, long long ld_row, long long ld_col, uint32_t* out,
                        int* bad_count, hipStream_t s) {
   PackedDims d = packed_dims(R, C);

@@ -150,6 +150,18 @@ nq_status nq_linear_fwd_group_profiled(const nq_layer* const* layers, int32_t L,
                                        void* const* events, int32_t n_events, int32_t* n_launches,
                                        int32_t* launch_dims);
 
+/* The transposed product (the backward pass through a binary layer that block
+ * reconstruction needs; hardwired.dev NanoQuant page, section "Trikrokovy
+ * pipeline", step 3).  W_hat^T = diag(s2) V diag(g) U^T diag(s1) has the same
+ * form with the roles swapped: U' = V, V' = U, s1' = s2, g' = g, s2' = s1.
+ * Writes that layer into dst (dst->m = src->n, dst->n = src->m, dst->r =
+ * src->r, same scale dtype, nq_layer_bytes(src->n, src->m, src->r) bytes, not
+ * overlapping src): header, bit-transposed factors (padding bits zero, as
+ * nq_pack_factors writes them) and the scales.  Then nq_linear_fwd(dst, dy)
+ * gives dx[b] = W_hat^T dy[b] for dy of shape B x src->m, on every path.
+ * BLOCKING: synchronises `stream`. */
+nq_status nq_transpose_layer(const nq_layer* src, const nq_layer* dst, nq_stream_t stream);
+
 /* Bytes of the static device scratch used by nq_linear_fwd_noalloc. */
 #define NQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 

@@ -25,6 +25,14 @@ the definition itself, with no approximation:
 * mode B (``linear_factored``): the same product evaluated right to left,
   y = s1 * (U (g * (V^T (s2 * x)))), in fp64; used where W_hat is too large.
 
+The backward product through the layer (same article, section "Trikrokovy
+pipeline", step 3: the factors are refined block by block by propagating
+gradients through the binarised layer) needs W_hat^T applied to an output
+gradient: for dy (B x m), dx = dy . W_hat (B x n), i.e. W_hat^T dy row by row:
+
+* ``linear_transposed_dense``: W_hat formed densely, dx = dy W_hat;
+* ``linear_transposed_factored``: dx = s2 * (V (g * (U^T (s1 * dy)))).
+
 Storage (same article and section, plus section 'Co znamena "sub-1-bit"'):
 a rank-r factorisation of an m x n matrix stores r(m+n) sign bits; the scale
 parameters counted here are the m + n + r entries of s1, g, s2 at
@@ -77,6 +85,25 @@ def linear_factored(x, U, V, s1, g, s2) -> np.ndarray:
     t = t * _f64(g)[None, :]                     # g * t
     z = t @ _f64(U).T                            # U t'              (B x m)
     return z * _f64(s1)[None, :]                 # s1 * z
+
+
+def linear_transposed_dense(dy, U, V, s1, g, s2) -> np.ndarray:
+    """dx = dy W_hat with W_hat formed densely.  dy is (B, m); dx is (B, n)."""
+    W = reconstruct_weight(U, V, s1, g, s2)
+    return _f64(dy) @ W
+
+
+def linear_transposed_factored(dy, U, V, s1, g, s2) -> np.ndarray:
+    """dx = s2 * (V (g * (U^T (s1 * dy)))), row by row of dy, in fp64."""
+    U = np.asarray(U)
+    V = np.asarray(V)
+    _check_signs(U, "U")
+    _check_signs(V, "V")
+    ds = _f64(dy) * _f64(s1)[None, :]            # s1 * dy           (B x m)
+    t = ds @ _f64(U)                             # U^T (s1 dy)       (B x r)
+    t = t * _f64(g)[None, :]                     # g * t
+    z = t @ _f64(V).T                            # V t'              (B x n)
+    return z * _f64(s2)[None, :]                 # s2 * z
 
 
 def bits_per_weight(m: int, n: int, r: int, scale_bits: int = 16) -> float:

@@ -210,3 +210,17 @@ def test_group_workspace_covers_the_fallback(L):
         need = max(L.nq_workspace_bytes_path(ctypes.byref(l), B, 0) for l in (q, k))
         assert L.nq_workspace_bytes_group(_group([q, k]), 2, B) <= need
         assert L.nq_workspace_bytes_group(_group([q, k]), 2, B) > 0
+
+
+def test_transpose_validation(L):
+    src = _layer(m=64, n=96, r=40)
+    good = _layer(m=96, n=64, r=40, blob=FAKE + (1 << 30))
+    t = lambda s, d: L.nq_transpose_layer(ctypes.byref(s) if s is not None else None,
+                                          ctypes.byref(d) if d is not None else None, None)
+    assert t(None, good) == nq.NQ_ERR_INVALID_ARG
+    assert t(src, None) == nq.NQ_ERR_INVALID_ARG
+    assert t(src, _layer(m=64, n=96, r=40, blob=FAKE + (1 << 30))) == nq.NQ_ERR_INVALID_ARG  # not the transpose
+    assert t(src, _layer(m=96, n=64, r=41, blob=FAKE + (1 << 30))) == nq.NQ_ERR_INVALID_ARG
+    assert t(src, _layer(m=96, n=64, r=40, dt=nq.NQ_F32, blob=FAKE + (1 << 30))) == nq.NQ_ERR_INVALID_ARG
+    assert t(src, _layer(m=96, n=64, r=40, blob=FAKE + 256)) == nq.NQ_ERR_INVALID_ARG  # blobs overlap
+    assert b"overlap" in L.nq_last_error()
