@@ -20,6 +20,7 @@ NQ_OK, NQ_ERR_INVALID_ARG, NQ_ERR_NOT_PM1, NQ_ERR_WORKSPACE, NQ_ERR_UNSUPPORTED,
     0, -1, -2, -3, -4, -5, -6
 NQ_F32, NQ_F16, NQ_BF16 = 0, 1, 2
 NQ_GROUP_MAX = 4  # layers per group call (include/nq.h)
+NQ_ENVELOPE_MAX = 4  # terms of a rank-l envelope (include/nq.h)
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "valu": 3, "decode": 4}
 
 _DT = {torch.float32: NQ_F32, torch.float16: NQ_F16, torch.bfloat16: NQ_BF16}
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(c_int), vp]),
         "nq_linear_fwd_noalloc": (c_int, [P, vp, c_int, vp, c_int, c_int, vp]),
         "nq_workspace_bytes_group": (c_size, [vp, c_int, c_int]),
+        "nq_workspace_bytes_envelope": (c_size, [P, c_int, c_int]),
+        "nq_linear_fwd_envelope": (c_int, [P, c_int, vp, vp, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
         "nq_linear_fwd_group": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
         "nq_linear_fwd_group_profiled": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp, vp, c_int,
                                                  ctypes.POINTER(c_int), vp]),
@@ -253,6 +256,26 @@ def linear_group_into_profiled(x: torch.Tensor, layers, ys, workspace: torch.Ten
                                               ctypes.cast(dims, ctypes.c_void_p)))
     k = min(nl.value, len(events) - 1)
     return [(dims[2 * i], dims[2 * i + 1]) for i in range(k)]
+
+
+def linear_envelope(x: torch.Tensor, layer: Layer, s1_env: torch.Tensor, s2_env: torch.Tensor,
+                    out_dtype: torch.dtype | None = None, stream=None) -> torch.Tensor:
+    """y = x W_hat^T with W_hat = sum_t diag(s1_env[t]) U diag(g) V^T diag(s2_env[t])
+    (rank-l envelope; U, V, g from the layer): B x terms <= 4."""
+    xx = x if x.dim() == 2 else x.view(1, -1)
+    B, env = xx.shape[0], s1_env.shape[0]
+    if s1_env.shape != (env, layer.m) or s2_env.shape != (env, layer.n) or \
+            s1_env.dtype != layer.scale_dtype or s2_env.dtype != layer.scale_dtype:
+        raise NQError(NQ_ERR_INVALID_ARG, "envelope scales must be (terms, m) and (terms, n) in the layer's dtype")
+    if not (xx.is_contiguous() and s1_env.is_contiguous() and s2_env.is_contiguous()):
+        raise NQError(NQ_ERR_INVALID_ARG, "x and the envelope scales must be contiguous")
+    y = torch.empty((B, layer.m), dtype=out_dtype or x.dtype, device=x.device)
+    ws = torch.empty(max(int(lib().nq_workspace_bytes_envelope(layer.ref, env, B)), 256), dtype=torch.uint8,
+                     device=x.device)
+    _check(lib().nq_linear_fwd_envelope(layer.ref, env, s1_env.data_ptr(), s2_env.data_ptr(), xx.data_ptr(),
+                                        _DT[xx.dtype], y.data_ptr(), _DT[y.dtype], B, ws.data_ptr(), ws.numel(),
+                                        _stream(stream)))
+    return y if x.dim() == 2 else y.view(-1)
 
 
 def linear_noalloc_into(x: torch.Tensor, layer: Layer, y: torch.Tensor, stream=None) -> torch.Tensor:

@@ -65,7 +65,7 @@ size_t plan_bytes(const nq_layer* L, int32_t B, int32_t path) {
     case NQ_PATH_VALU: return nq::valu_plan(L->m, L->n, L->r).bytes;
     case NQ_PATH_GEMM: return nq::gemm_plan(L->m, L->n, L->r, B).bytes;
     case NQ_PATH_DECODE: {
-      nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B);
+      nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype));
       return p.ok ? p.bytes : 0;
     }
   }
@@ -222,13 +222,13 @@ size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path) {
   if (path == NQ_PATH_AUTO) return nq_workspace_bytes(L, B);
   if (path == NQ_PATH_GEMV && B > 16) return 0;
   if (path == NQ_PATH_VALU && B != 1) return 0;
-  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B).ok) return 0;
+  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype)).ok) return 0;
   if (path < NQ_PATH_AUTO || path > NQ_PATH_DECODE) return 0;
   return plan_bytes(L, B, path);
 }
 
 static int32_t auto_path(const nq_layer* L, int32_t B) {
-  if (B <= 4 && nq::dec_plan(L->m, L->n, L->r, B).ok) return NQ_PATH_DECODE;
+  if (B <= 4 && nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype)).ok) return NQ_PATH_DECODE;
   return B <= 16 ? NQ_PATH_GEMV : NQ_PATH_GEMM;
 }
 
@@ -262,7 +262,7 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   if (path == NQ_PATH_AUTO) path = auto_path(L, B);
   if (path == NQ_PATH_GEMV && B > 16) return fail(NQ_ERR_UNSUPPORTED, "gemv path takes B <= 16 (got %d)", B);
   if (path == NQ_PATH_VALU && B != 1) return fail(NQ_ERR_UNSUPPORTED, "valu path takes B == 1 (got %d)", B);
-  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B).ok)
+  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype)).ok)
     return fail(NQ_ERR_UNSUPPORTED, "decode path takes B <= 4 and a rank whose image fits in LDS (B=%d r=%d)", B,
                 L->r);
   const size_t need = plan_bytes(L, B, path);
@@ -293,27 +293,121 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   switch (path) {
     case NQ_PATH_GEMV: e = nq::gemv_forward(a, nq::gemv_plan(a.m, a.n, a.r, B)); break;
     case NQ_PATH_VALU: e = nq::valu_forward(a, nq::valu_plan(a.m, a.n, a.r)); break;
-    case NQ_PATH_DECODE: e = nq::dec_forward(a, nq::dec_plan(a.m, a.n, a.r, B)); break;
+    case NQ_PATH_DECODE: e = nq::dec_forward(a, nq::dec_plan(a.m, a.n, a.r, B, scale_bytes(a.scale_dtype))); break;
     default: e = nq::gemm_forward(a, nq::gemm_plan(a.m, a.n, a.r, B)); break;
   }
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return ok();
 }
 
-// ------------------------------------------------------------------ layer groups
-static_assert(NQ_GROUP_MAX == nq::GROUP_MAX, "one group size for the header and the kernels");
 static bool spans_overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// ------------------------------------------------------------------ rank-l envelope
+// The env scale-vector pairs are first copied into the workspace, each row
+// padded (s1 rows to 16 elements, s2 rows to 8) so that the kernels' whole-word
+// reads never leave the buffer; the forward's own workspace follows.
+struct EnvLayout {
+  size_t s1_pitch, s2_pitch;  // bytes between rows
+  size_t off_s1, off_s2, off_fwd, bytes;
+};
+
+static EnvLayout env_layout(const nq_layer* L, int32_t env, size_t fwd_bytes) {
+  const int sb = scale_bytes(L->scale_dtype);
+  EnvLayout e;
+  e.s1_pitch = (size_t)(L->m + 15) / 16 * 16 * sb;
+  e.s2_pitch = (size_t)(L->n + 7) / 8 * 8 * sb;
+  e.off_s1 = 0;
+  e.off_s2 = (e.off_s1 + env * e.s1_pitch + 255) / 256 * 256;
+  e.off_fwd = (e.off_s2 + env * e.s2_pitch + 255) / 256 * 256;
+  e.bytes = e.off_fwd + fwd_bytes;
+  return e;
+}
+
+static nq::DecPlan env_plan(const nq_layer* L, int32_t env, int32_t B) {
+  nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B * env, scale_bytes(L->scale_dtype));
+  if (!p.rows2) p.ok = false;  // the envelope sum lives in the row-split stage 2
+  return p;
+}
+
+size_t nq_workspace_bytes_envelope(const nq_layer* L, int32_t env, int32_t B) {
+  if (check_layer(L) || env < 1 || env > NQ_ENVELOPE_MAX || B < 1 || B * env > 4) return 0;
+  const nq::DecPlan p = env_plan(L, env, B);
+  return p.ok ? env_layout(L, env, p.bytes).bytes : 0;
+}
+
+nq_status nq_linear_fwd_envelope(const nq_layer* L, int32_t env, const void* s1_env, const void* s2_env,
+                                 const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
+                                 void* workspace, size_t workspace_bytes, nq_stream_t stream) {
+  nq_status st = check_layer(L);
+  if (st) return st;
+  if (env < 1 || env > NQ_ENVELOPE_MAX)
+    return fail(NQ_ERR_INVALID_ARG, "envelope of %d terms (1..%d)", env, NQ_ENVELOPE_MAX);
+  if (B < 0 || B > MAX_BATCH) return fail(NQ_ERR_INVALID_ARG, "batch %d out of range 0..%d", B, MAX_BATCH);
+  const int xb = act_bytes(x_dtype), yb = act_bytes(y_dtype), sb = scale_bytes(L->scale_dtype);
+  if (!xb) return fail(NQ_ERR_INVALID_ARG, "x_dtype %d is not NQ_BF16 or NQ_F32", x_dtype);
+  if (!yb) return fail(NQ_ERR_INVALID_ARG, "y_dtype %d is not NQ_BF16 or NQ_F32", y_dtype);
+  if (B == 0) return ok();
+  if (!x || !y || !s1_env || !s2_env) return fail(NQ_ERR_INVALID_ARG, "x, y, s1_env and s2_env must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(x) % xb || reinterpret_cast<uintptr_t>(y) % yb ||
+      reinterpret_cast<uintptr_t>(s1_env) % sb || reinterpret_cast<uintptr_t>(s2_env) % sb)
+    return fail(NQ_ERR_INVALID_ARG, "x, y or an envelope scale array is not aligned to its element size");
+  if (spans_overlap(x, (size_t)B * L->n * xb, y, (size_t)B * L->m * yb))
+    return fail(NQ_ERR_INVALID_ARG, "x and y overlap");
+  if (B * env > 4)
+    return fail(NQ_ERR_UNSUPPORTED, "the envelope path takes B x terms <= 4 (got %d x %d)", B, env);
+  const nq::DecPlan p = env_plan(L, env, B);
+  if (!p.ok) return fail(NQ_ERR_UNSUPPORTED, "no envelope plan for m=%d n=%d r=%d", L->m, L->n, L->r);
+  const EnvLayout e = env_layout(L, env, p.bytes);
+  if (workspace_bytes < e.bytes)
+    return fail(NQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
+                e.bytes);
+  if (!workspace) return fail(NQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(NQ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t he = hipMemcpy2DAsync(ws + e.off_s1, e.s1_pitch, s1_env, (size_t)L->m * sb, (size_t)L->m * sb, env,
+                                   hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess)
+    he = hipMemcpy2DAsync(ws + e.off_s2, e.s2_pitch, s2_env, (size_t)L->n * sb, (size_t)L->n * sb, env,
+                          hipMemcpyDeviceToDevice, s);
+  if (he != hipSuccess) return hip_fail(he, "envelope scale copy");
+  nq::FwdArgs a;
+  a.m = L->m;
+  a.n = L->n;
+  a.r = L->r;
+  a.B = B * env;
+  a.scale_dtype = L->scale_dtype;
+  a.x_dtype = x_dtype;
+  a.y_dtype = y_dtype;
+  a.blob = static_cast<const uint8_t*>(L->blob);
+  a.x = x;
+  a.y = y;
+  a.ws = ws + e.off_fwd;
+  a.ws_bytes = workspace_bytes - e.off_fwd;
+  a.stream = s;
+  a.env = env;
+  a.s1_env = ws + e.off_s1;
+  a.s2_env = ws + e.off_s2;
+  a.s1_env_stride = (int)(e.s1_pitch / sb);
+  a.s2_env_stride = (int)(e.s2_pitch / sb);
+  he = nq::dec_forward(a, p);
+  if (he != hipSuccess) return hip_fail(he, "envelope forward launch");
+  return ok();
+}
+
+// ------------------------------------------------------------------ layer groups
+static_assert(NQ_GROUP_MAX == nq::GROUP_MAX, "one group size for the header and the kernels");
 static nq::GroupPlan group_plan_of(const nq_layer* const* layers, int32_t L, int32_t B) {
   int m[NQ_GROUP_MAX], r[NQ_GROUP_MAX];
   for (int l = 0; l < L; l++) {
     m[l] = layers[l]->m;
     r[l] = layers[l]->r;
   }
-  return nq::group_plan(m, r, L, layers[0]->n, B);
+  return nq::group_plan(m, r, L, layers[0]->n, B, scale_bytes(layers[0]->scale_dtype));
 }
 
 static nq_status check_group(const nq_layer* const* layers, int32_t L) {

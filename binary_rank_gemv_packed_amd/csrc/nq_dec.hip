@@ -24,6 +24,7 @@
 // so a prologue costs one memory round trip and the encoder never waits for
 // the weight stream.
 #include <climits>
+#include <type_traits>
 
 #include "nq_common.h"
 #include "nq_internal.h"
@@ -159,6 +160,13 @@ __device__ __forceinline__ void chunk_pos(int t, int KL, int& b, int& ktl) {
   ktl = t - b * KL;
 }
 
+// Rank-l envelope: internal batch row b (< 4) is input row b / env under
+// scale row b % env, for env in 1..4 (without a division).
+__device__ __forceinline__ void env_split(int b, int env, int& xr, int& sr) {
+  xr = env == 1 ? b : (env == 2 ? b >> 1 : (env == 3 ? (b >= 3 ? 1 : 0) : 0));
+  sr = b - xr * env;
+}
+
 // ------------------------------------------------------------------ sources
 template <typename T> __device__ inline float ld_f32(const T* p, size_t i);
 template <> __device__ inline float ld_f32<float>(const float* p, size_t i) { return p[i]; }
@@ -206,18 +214,21 @@ struct XPass {
 
   // x rows start every xstride elements, 16-byte aligned, xstride a multiple
   // of 8; lanes past the last chunk load a copy of it.
+  // With an envelope of env terms, batch row b reads x row b / env and s2 row
+  // b % env (s2 rows s2_stride apart).
   __device__ __forceinline__ void load(const XT* __restrict__ x, int xstride, const ST* __restrict__ s2, int n,
-                                       int kt0, int KL, int base) {
+                                       int kt0, int KL, int base, int env, int s2_stride) {
     const int total = BB * KL * 16, nt = blockDim.x;
 #pragma unroll
     for (int c = 0; c < CPT; c++) {
       const int ci = base + c * nt + threadIdx.x;
       const int cc = ci < total ? ci : total - 1;
-      int b, ktl;
+      int b, ktl, xr, sr;
       chunk_pos<BB>(cc >> 4, KL, b, ktl);
+      env_split(b, env, xr, sr);
       const int k = (kt0 + ktl) * 128 + 8 * (cc & 15);
-      raw_words(x + (size_t)b * xstride, k, n, rx[c]);
-      raw_words(s2, k, n, rs[c]);
+      raw_words(x + (size_t)xr * xstride, k, n, rx[c]);
+      raw_words(s2 + (size_t)sr * s2_stride, k, n, rs[c]);
     }
   }
 
@@ -566,6 +577,8 @@ struct S1Args {
   float* part;
   int Rpad;
   int red_off;         // byte offset of the reduction buffer in LDS
+  int env = 1;         // envelope terms: batch row b = input row b / env under s2 row b % env
+  int s2_stride = 0;   // elements between s2 rows of an envelope
 };
 
 // The work of one stage-1 workgroup: row group `rowgroup` (RM row tiles) of
@@ -591,11 +604,11 @@ __device__ __forceinline__ void s1_body(const S1Args& a, int rowgroup, int split
   XPass<XT, ST, BB> xp;
   // the prologue's loads go out first, then the weight stream; the encoder
   // waits for the prologue's loads only
-  xp.load(x, a.xstride, s2, a.n, kt0, KLr, 0);
+  xp.load(x, a.xstride, s2, a.n, kt0, KLr, 0, a.env, a.s2_stride);
   wave_load<RM>(a.vt, a.KT, a.RT, ww, lane);
   xp.encode(a.n, KLr, kt0, CW, 0, li);
   for (int base = per_pass; base < total; base += per_pass) {
-    xp.load(x, a.xstride, s2, a.n, kt0, KLr, base);
+    xp.load(x, a.xstride, s2, a.n, kt0, KLr, base, a.env, a.s2_stride);
     xp.encode(a.n, KLr, kt0, CW, base, li);
   }
   __syncthreads();
@@ -661,6 +674,8 @@ struct S2Args {
   int ydt, m;
   int red_off;
   int s1_off;  // byte offset of the staged output scales in LDS
+  int env = 1;         // envelope terms summed into one output row (row-split kernel only)
+  int s1_stride = 0;   // elements between s1 rows of an envelope
 };
 
 // The work of one stage-2 workgroup: row group `rowgroup` (RM row tiles).
@@ -737,6 +752,105 @@ __device__ __forceinline__ void s2_body(const S2Args& a, int rowgroup, uint8_t* 
   });
 }
 
+// Stage 2 with the waves of a workgroup on different rows: every wave takes
+// RM row tiles over the whole rank (RM x quads <= 16), so no partial results
+// cross waves and the workgroup of W waves shares one encoded t' among W x RM
+// row tiles (fewer workgroups, so fewer copies of t' to read and encode).
+// Row group `rowgroup` = row tiles [rowgroup * W * RM, + W * RM).
+template <typename ST, int BB, int RM, int SM>
+__device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint8_t* lds) {
+  constexpr int CW = 4 * BB;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  WaveWork<RM> ww;
+  ww.rt0 = (rowgroup * W + wave) * RM;
+  const int RG = min(RM, a.RT - ww.rt0);  // rows of this wave (<= 0: none; its loads are clamped)
+  ww.qa = 0;
+  ww.qb = (a.KT + 3) >> 2;
+  const Img li = img_at(lds, a.KT, CW);
+  const ST* g = reinterpret_cast<const ST*>(a.g);
+  const ST* s1 = reinterpret_cast<const ST*>(a.s1);
+  const int per_pass = TPass<ST, SM, BB>::CPT * blockDim.x, total = BB * a.KT * 16;
+  TPass<ST, SM, BB> tp;
+  tp.load(a.part, a.S1, a.Rpad1, g, a.r, a.KT, 0);  // prologue loads first, then the weight stream
+  wave_load<RM>(a.u, a.KT, a.RT, ww, lane);
+  // output scales of this lane's four rows in each row tile (one word per tile,
+  // clamped into the layer; used only for rows < m)
+  Raw8<ST> s1w[RM];
+  const int c = lane & 15, b = c >> 2;
+  int ob, sr;  // output row and envelope term of this lane's batch column
+  env_split(b < BB ? b : BB - 1, a.env, ob, sr);
+  const ST* s1r = s1 + (size_t)sr * a.s1_stride;
+#pragma unroll
+  for (int r = 0; r < RM; r++) {
+    const int rt = min(ww.rt0 + r, a.RT - 1);
+    const int row4 = rt * 16 + 4 * (lane >> 4);
+    if constexpr (sizeof(ST) == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(s1r + row4);
+      s1w[r].w[0] = uint4{v.x, v.y, 0u, 0u};
+    } else {
+      s1w[r].w[0] = *reinterpret_cast<const uint4*>(s1r + row4);
+    }
+  }
+  tp.encode(a.S1, a.r, a.KT, CW, 0, li);
+  for (int base = per_pass; base < total; base += per_pass) {
+    tp.load(a.part, a.S1, a.Rpad1, g, a.r, a.KT, base);
+    tp.encode(a.S1, a.r, a.KT, CW, base, li);
+  }
+  __syncthreads();
+  if (RG <= 0) return;
+  float S[4];
+  range_sums(li.sum, a.KT, BB, lane, S);
+  const LaneImg<CW> im(li, lane);
+  v4f acc[RM];
+#pragma unroll
+  for (int r = 0; r < RM; r++) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+  wave_mma<CW, RM>(a.u, a.KT, a.RT, ww, im, 0, lane, acc);
+  // columns 4b hold batch row b; with an envelope the env rows of one output
+  // row are summed across lanes 4 and 8 apart (columns past the batch add 0)
+  const bool valid = (c & 3) == 0 && b < BB && sr == 0;
+#pragma unroll
+  for (int r = 0; r < RM; r++) {
+    float z[4];
+    finish_acc(acc[r], S, lane, z);
+    if (r < RG) {
+      ST sc[4];
+      __builtin_memcpy(sc, s1w[r].w, sizeof(sc));
+      float yv[4];
+#pragma unroll
+      for (int v = 0; v < 4; v++) yv[v] = ld_f32(sc, v) * z[v];
+      if (a.env > 1) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          yv[v] = b < BB ? yv[v] : 0.0f;
+          yv[v] += __shfl_xor(yv[v], 4);
+          if (a.env > 2) yv[v] += __shfl_xor(yv[v], 8);
+        }
+      }
+      if (valid) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const int row = (ww.rt0 + r) * 16 + 4 * (lane >> 4) + v;
+          if (row < a.m) {
+            const size_t yi = (size_t)ob * a.m + row;
+            if (a.ydt == 0) reinterpret_cast<float*>(a.y)[yi] = yv[v];
+            else reinterpret_cast<uint16_t*>(a.y)[yi] = f32_to_bf16(yv[v]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// BIG: more than 8 waves per workgroup (launch bound 1024 threads, so at most
+// 128 VGPRs: only the shapes the plan allows it for fit without spilling).
+template <typename ST, int BB, int RM, int SM, bool BIG>
+__global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_kernel(S2Args a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  s2_rows_body<ST, BB, RM, SM>(a, blockIdx.x, lds);
+}
+
 template <typename ST, bool FUSED, int BB, int RM, int SM>
 __global__ void __launch_bounds__(512) dec_s2_kernel(S2Args a) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -758,6 +872,17 @@ __global__ void __launch_bounds__(512) dec_s2_group_kernel(S2Group g) {
   for (int i = 0; i < MAX_GROUP - 1; i++) l += bx >= g.wg_end[i] ? 1 : 0;
   const int begin = l == 0 ? 0 : g.wg_end[l - 1];
   s2_body<ST, true, BB, RM, SM>(g.l[l], bx - begin, lds);
+}
+
+template <typename ST, int BB, int RM, int SM, bool BIG>
+__global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_group_kernel(S2Group g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int bx = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_GROUP - 1; i++) l += bx >= g.wg_end[i] ? 1 : 0;
+  const int begin = l == 0 ? 0 : g.wg_end[l - 1];
+  s2_rows_body<ST, BB, RM, SM>(g.l[l], bx - begin, lds);
 }
 
 }  // namespace
@@ -786,7 +911,27 @@ static bool pick_shape(int RT, int splits, int quads, int minwg, int* RM, int* K
   return false;
 }
 
-DecPlan dec_plan(int m, int n, int r, int B) {
+// Stage 2 with row-split waves (see s2_rows_body) when every row tile's quads
+// fit one wave's 16-quad buffer: RM row tiles per wave, W waves per workgroup.
+// W is sized so that about 160 workgroups cover the rows and so that the
+// prologue (2 chunks per thread per pass) takes one pass; more than 8 waves
+// only where the kernel fits 128 VGPRs (RM <= 2, S1 <= 2 partials, B = 1,
+// 2-byte scales).
+static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_bytes, int* RM, int* W) {
+  if (quads > 16) return false;
+  int rm = 8;
+  while (rm > 1 && rm * quads > 16) rm /= 2;
+  int w = ceil_div(RT, rm * 160);
+  const int w_pass = ceil_div(chunks, 2 * 64);
+  w = w > w_pass ? w : w_pass;
+  const int wmax = (rm <= 2 && S1 <= 2 && B == 1 && scale_bytes == 2) ? 16 : 8;
+  w = w < 1 ? 1 : (w > wmax ? wmax : w);
+  *RM = rm;
+  *W = w;
+  return true;
+}
+
+DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes) {
   DecPlan p{};
   p.ok = false;
   if (B < 1 || B > DEC_MAX_B) return p;
@@ -812,11 +957,22 @@ DecPlan dec_plan(int m, int n, int r, int B) {
     s = s > smax ? smax : s;
     s = s > quads1 ? quads1 : s;
     s = s < 1 ? 1 : s;
+    // stage 2 folds the partial vectors into its prologue when S1 * B <= 4
+    const int s_fold = 4 / B;
+    s = s > s_fold ? s_fold : s;
     const int s_lds = ceil_div(p.KT1, klmax);
     if (s < s_lds) s = s_lds;
-    if (s == 3) s = 4;  // stage 2 reads 1, 2 or 4 partial vectors
+    if (s == 3) s = B == 1 ? 4 : 2;  // stage 2 reads 1, 2 or 4 partial vectors
+    if (s < s_lds) s = s_lds;
     p.KL1 = 4 * ceil_div(ceil_div(p.KT1, s), 4);
     p.S1 = ceil_div(p.KT1, p.KL1);
+    if (p.S1 == 3) {  // rounding KL1 to whole quads gave 3 splits: take 2 if they fit LDS
+      const int kl2 = 4 * ceil_div(ceil_div(p.KT1, 2), 4);
+      if (kl2 <= klmax) {
+        p.KL1 = kl2;
+        p.S1 = ceil_div(p.KT1, p.KL1);
+      }
+    }
     if (!pick_shape(p.RT1, p.S1, ceil_div(p.KL1, 4), MIN_WG, &p.RG1, &p.KS1)) return p;
   }
   p.QM1 = ceil_div(ceil_div(p.KL1, 4), p.KS1);
@@ -844,6 +1000,16 @@ DecPlan dec_plan(int m, int n, int r, int B) {
   p.lds2 = p.red2 + red_bytes + S1_LDS_BYTES;
   if (p.lds2 > LDS_S2) return p;
   p.fused_mid = p.S1 * B <= 4 && p.S1 != 3;
+  p.rows2 = false;
+  {
+    int rm, w;
+    if (p.fused_mid && pick_rows(p.RT2, quads2, B * p.KT2 * 16, p.S1, B, scale_bytes, &rm, &w) && p.KT2 * tb <= LDS_S2) {
+      p.rows2 = true;
+      p.RG2 = rm;
+      p.KS2 = w;
+      p.lds2 = p.KT2 * tb;
+    }
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -869,6 +1035,40 @@ static void launch_s2(int RG, dim3 g, dim3 b, size_t lds, hipStream_t st, const 
   }
 }
 
+template <typename ST, int BB, int SM, typename K>
+static void launch_rows_t(int RM, bool big, dim3 g, dim3 b, size_t lds, hipStream_t st, const K& k) {
+  constexpr bool GROUP = std::is_same<K, S2Group>::value;
+#define NQ_ROWS(R, BIGV)                                                                                    \
+  do {                                                                                                      \
+    if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k); \
+    else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k);                   \
+  } while (0)
+  if constexpr (BB == 1 && SM <= 2 && sizeof(ST) == 2) {
+    if (big) {  // the shapes with more than 8 waves (RM <= 2, see pick_rows)
+      if (RM == 2) NQ_ROWS(2, true);
+      else NQ_ROWS(1, true);
+      return;
+    }
+  }
+  switch (RM) {
+    case 8: NQ_ROWS(8, false); break;
+    case 4: NQ_ROWS(4, false); break;
+    case 2: NQ_ROWS(2, false); break;
+    default: NQ_ROWS(1, false); break;
+  }
+#undef NQ_ROWS
+}
+
+template <typename ST, int BB, int SM>
+static void launch_s2_rows(int RM, int W, dim3 g, dim3 b, size_t lds, hipStream_t st, const S2Args& k) {
+  launch_rows_t<ST, BB, SM>(RM, W > 8, g, b, lds, st, k);
+}
+
+template <typename ST, int BB, int SM>
+static void launch_s2_rows_group(int RM, int W, dim3 g, dim3 b, size_t lds, hipStream_t st, const S2Group& k) {
+  launch_rows_t<ST, BB, SM>(RM, W > 8, g, b, lds, st, k);
+}
+
 template <typename ST, int BB, int SM>
 static void launch_s2_group(int RG, dim3 g, dim3 b, size_t lds, hipStream_t st, const S2Group& k) {
   switch (RG) {
@@ -885,9 +1085,13 @@ static hipError_t dec_forward_t(const FwdArgs& a, const DecPlan& p) {
   BlobLayout L = blob_layout(a.m, a.n, a.r, sb);
   const uint32_t* U = reinterpret_cast<const uint32_t*>(a.blob + L.off_u);
   const uint32_t* Vt = reinterpret_cast<const uint32_t*>(a.blob + L.off_vt);
-  const ST* s1 = reinterpret_cast<const ST*>(a.blob + L.off_s1);
+  // an envelope of env terms runs as env x B internal batch rows (B input and
+  // output rows) with the scale vectors of each term from s1_env / s2_env
+  const bool envl = a.env > 1;
+  const ST* s1 = reinterpret_cast<const ST*>(envl ? a.s1_env : a.blob + L.off_s1);
   const ST* g = reinterpret_cast<const ST*>(a.blob + L.off_g);
-  const ST* s2 = reinterpret_cast<const ST*>(a.blob + L.off_s2);
+  const ST* s2 = reinterpret_cast<const ST*>(envl ? a.s2_env : a.blob + L.off_s2);
+  const int xrows = a.B / a.env;
   hipStream_t st = a.stream;
   float* part = reinterpret_cast<float*>(a.ws + p.off_part);
   uint8_t* img2 = a.ws + p.off_img2;
@@ -897,14 +1101,16 @@ static hipError_t dec_forward_t(const FwdArgs& a, const DecPlan& p) {
   if (!xvec) {  // rows not 16-byte aligned: an aligned, zero-padded copy first
     xstride = align_up(a.n, 8);
     XT* xp = reinterpret_cast<XT*>(a.ws + p.off_xpad);
-    const int tot = a.B * xstride;
+    const int tot = xrows * xstride;
     mark(a, dim3(ceil_div(tot, 256)), dim3(256));
     hipLaunchKernelGGL((dec_xpad_kernel<XT>), dim3(ceil_div(tot, 256)), dim3(256), 0, st,
-                       reinterpret_cast<const XT*>(a.x), a.n, a.B, xstride, xp);
+                       reinterpret_cast<const XT*>(a.x), a.n, xrows, xstride, xp);
     x = xp;
   }
 
   S1Args k1{Vt, p.RT1, p.KT1, p.KL1, p.RG1, p.KS1, x, s2, a.n, xstride, p.CW, a.B, part, p.Rpad1, (int)p.red1};
+  k1.env = a.env;
+  k1.s2_stride = envl ? a.s2_env_stride : 0;
   {
     dim3 g1(ceil_div(p.RT1, p.RG1), p.S1), b1(64 * p.KS1);
     mark(a, g1, b1);
@@ -923,9 +1129,15 @@ static hipError_t dec_forward_t(const FwdArgs& a, const DecPlan& p) {
   }
   S2Args k2{U, p.RT2, p.KT2, p.RG2, p.KS2, p.fused_mid ? nullptr : img2, part, p.S1, p.Rpad1, a.r, g, p.CW, a.B,
             s1, a.scale_dtype, a.y, a.y_dtype == 0 ? 0 : 2, a.m, (int)p.red2, (int)(p.lds2 - S1_LDS_BYTES)};
-  dim3 g2(ceil_div(p.RT2, p.RG2)), b2(64 * p.KS2);
+  k2.env = a.env;
+  k2.s1_stride = envl ? a.s1_env_stride : 0;
+  dim3 g2(ceil_div(p.RT2, p.RG2 * (p.rows2 ? p.KS2 : 1))), b2(64 * p.KS2);
   mark(a, g2, b2);
-  if (p.fused_mid) {
+  if (p.rows2) {
+    if (p.S1 == 1) launch_s2_rows<ST, BB, 1>(p.RG2, p.KS2, g2, b2, p.lds2, st, k2);
+    else if (p.S1 == 2) launch_s2_rows<ST, BB, (BB <= 2 ? 2 : 1)>(p.RG2, p.KS2, g2, b2, p.lds2, st, k2);
+    else launch_s2_rows<ST, BB, (BB == 1 ? 4 : 1)>(p.RG2, p.KS2, g2, b2, p.lds2, st, k2);
+  } else if (p.fused_mid) {
     // splits read by the prologue: 1, 2 or 4 (S1 * B <= 4)
     if (p.S1 == 1) launch_s2<ST, true, BB, 1>(p.RG2, g2, b2, p.lds2, st, k2);
     else if (p.S1 == 2) launch_s2<ST, true, BB, (BB <= 2 ? 2 : 1)>(p.RG2, g2, b2, p.lds2, st, k2);
@@ -947,7 +1159,7 @@ static hipError_t dec_forward_b(const FwdArgs& a, const DecPlan& p) {
   }
 }
 
-GroupPlan group_plan(const int* m, const int* r, int L, int n, int B) {
+GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_bytes) {
   GroupPlan p{};
   p.ok = false;
   if (L < 1 || L > GROUP_MAX || B < 1 || B > DEC_MAX_B) return p;
@@ -986,6 +1198,13 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B) {
     if (s == 3) s = 4;
     p.KL1 = 4 * ceil_div(ceil_div(p.KT1, s), 4);
     p.S1 = ceil_div(p.KT1, p.KL1);
+    if (p.S1 == 3) {  // rounding KL1 to whole quads gave 3 splits: take 2 if they fit LDS
+      const int kl2 = 4 * ceil_div(ceil_div(p.KT1, 2), 4);
+      if (kl2 <= klmax) {
+        p.KL1 = kl2;
+        p.S1 = ceil_div(p.KT1, p.KL1);
+      }
+    }
     if (!pick_shape(rt1_sum, p.S1, ceil_div(p.KL1, 4), MIN_WG, &p.RG1, &p.KS1)) return p;
   }
   if (p.S1 * B > 4 || p.S1 == 3) return p;  // stage 2 folds the partial sums in its prologue
@@ -1006,11 +1225,22 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B) {
   p.red2 = align_up((size_t)kt2max * tb, 16);
   p.lds2 = p.red2 + red_bytes + S1_LDS_BYTES;
   if (p.lds2 > LDS_S2) return p;
+  p.rows2 = false;
+  {
+    int rm, w;
+    if (pick_rows(rt2_sum, quads2, B * kt2max * 16, p.S1, B, scale_bytes, &rm, &w)) {
+      p.rows2 = true;
+      p.RG2 = rm;
+      p.KS2 = w;
+      p.lds2 = kt2max * tb;
+    }
+  }
+  const int rows_per_wg2 = p.rows2 ? p.RG2 * p.KS2 : p.RG2;
   int e1 = 0, e2 = 0;
   for (int l = 0; l < GROUP_MAX; l++) {
     if (l < L) {
       e1 += ceil_div(p.RT1[l], p.RG1);
-      e2 += ceil_div(p.RT2[l], p.RG2);
+      e2 += ceil_div(p.RT2[l], rows_per_wg2);
       p.wg1_end[l] = e1;
       p.wg2_end[l] = e2;
     } else {
@@ -1076,7 +1306,11 @@ static hipError_t group_forward_t(const GroupArgs& a, const GroupPlan& p) {
   const dim3 grid2(p.wg2_end[a.L - 1]), b2(64 * p.KS2);
   mark(fa, grid2, b2);
   // splits folded by the prologue: 1, 2 or 4 (S1 * B <= 4)
-  if (p.S1 == 1) launch_s2_group<ST, BB, 1>(p.RG2, grid2, b2, p.lds2, st, g2);
+  if (p.rows2) {
+    if (p.S1 == 1) launch_s2_rows_group<ST, BB, 1>(p.RG2, p.KS2, grid2, b2, p.lds2, st, g2);
+    else if (p.S1 == 2) launch_s2_rows_group<ST, BB, (BB <= 2 ? 2 : 1)>(p.RG2, p.KS2, grid2, b2, p.lds2, st, g2);
+    else launch_s2_rows_group<ST, BB, (BB == 1 ? 4 : 1)>(p.RG2, p.KS2, grid2, b2, p.lds2, st, g2);
+  } else if (p.S1 == 1) launch_s2_group<ST, BB, 1>(p.RG2, grid2, b2, p.lds2, st, g2);
   else if (p.S1 == 2) launch_s2_group<ST, BB, (BB <= 2 ? 2 : 1)>(p.RG2, grid2, b2, p.lds2, st, g2);
   else launch_s2_group<ST, BB, (BB == 1 ? 4 : 1)>(p.RG2, grid2, b2, p.lds2, st, g2);
   mark(fa);

@@ -41,6 +41,13 @@ struct FwdArgs {
   size_t ws_bytes;
   hipStream_t stream;
   LaunchMarks* marks = nullptr;  // null: no timing marks
+  // rank-l envelope (decode path, row-split stage 2 only): B counts env x the
+  // input rows; the env scale-vector pairs are s1_env (env x m), s2_env (env x n)
+  int env = 1;
+  const void* s1_env = nullptr;
+  const void* s2_env = nullptr;
+  int s1_env_stride = 0, s2_env_stride = 0;  // elements between rows; a row may be read
+                                             // in whole words up to 16 (s1) / 8 (s2) past its end
 };
 
 // Before each launch (with its grid and block) and once after the last one
@@ -76,6 +83,7 @@ hipError_t gemv_forward(const FwdArgs& a, const GemvPlan& p);
 // column parts per workgroup.  fused_mid: stage 2 builds the image of t' itself.
 struct DecPlan {
   bool ok, fused_mid;
+  bool rows2;  // stage 2 with row-split waves: RG2 row tiles per wave, KS2 waves per workgroup
   int B, CW;
   int RT1, KT1, RG1, KL1, S1, KS1, Rpad1;
   int RT2, KT2, RG2, KS2;
@@ -84,7 +92,7 @@ struct DecPlan {
   size_t off_img1, off_part, off_img2, off_xpad;
   size_t bytes;
 };
-DecPlan dec_plan(int m, int n, int r, int B);
+DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes);  // scale_bytes: 2 (fp16) or 4
 hipError_t dec_forward(const FwdArgs& a, const DecPlan& p);
 
 // Several layers that share x (same n, scale dtype, batch <= 4) in two
@@ -95,13 +103,14 @@ struct GroupPlan {
   int L, B, CW;
   int KT1, KL1, S1, RG1, KS1;   // stage 1, common to the layers
   int RG2, KS2;                 // stage 2, common to the layers
+  bool rows2;                   // stage 2 with row-split waves (RG2 rows per wave, KS2 waves)
   int RT1[GROUP_MAX], Rpad1[GROUP_MAX], RT2[GROUP_MAX], KT2[GROUP_MAX];
   int wg1_end[GROUP_MAX], wg2_end[GROUP_MAX];  // cumulative workgroups per layer
   size_t lds1, lds2, red1, red2;
   size_t off_part[GROUP_MAX], off_xpad;
   size_t bytes;
 };
-GroupPlan group_plan(const int* m, const int* r, int L, int n, int B);
+GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_bytes);
 
 struct GroupArgs {
   int L, n, B;

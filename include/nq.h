@@ -162,6 +162,23 @@ nq_status nq_linear_fwd_group_profiled(const nq_layer* const* layers, int32_t L,
  * BLOCKING: synchronises `stream`. */
 nq_status nq_transpose_layer(const nq_layer* src, const nq_layer* dst, nq_stream_t stream);
 
+/* Rank-l envelope (the MDBF variant; hardwired.dev NanoQuant page, section
+ * "Kontext: co existuje kolem", MDBF: the single magnitude profile of DBF,
+ * which is the form of nq_linear_fwd, replaced by an envelope of rank l).
+ * Reading: W_hat = sum_t diag(s1_t) U diag(g) V^T diag(s2_t), t < env, with
+ * U, V^T and g from the layer's blob and the env scale-vector pairs given here:
+ * s1_env (env x m) and s2_env (env x n), device, row-major, scale dtype of the
+ * layer (the blob's own s1 and s2 are not used).  y = x W_hat^T, x B x n, y
+ * B x m.  The sign bits are read once for all terms (the env terms run as
+ * extra batch rows and are summed in registers), so B x env <= 4, env <=
+ * NQ_ENVELOPE_MAX; otherwise NQ_ERR_UNSUPPORTED.  The workspace holds padded
+ * copies of the scale pairs plus the forward's own scratch. */
+#define NQ_ENVELOPE_MAX 4
+size_t nq_workspace_bytes_envelope(const nq_layer* L, int32_t env, int32_t B);
+nq_status nq_linear_fwd_envelope(const nq_layer* L, int32_t env, const void* s1_env, const void* s2_env,
+                                 const void* x, int32_t x_dtype, void* y, int32_t y_dtype, int32_t B,
+                                 void* workspace, size_t workspace_bytes, nq_stream_t stream);
+
 /* Bytes of the static device scratch used by nq_linear_fwd_noalloc. */
 #define NQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 

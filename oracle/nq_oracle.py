@@ -33,6 +33,18 @@ gradient: for dy (B x m), dx = dy . W_hat (B x n), i.e. W_hat^T dy row by row:
 * ``linear_transposed_dense``: W_hat formed densely, dx = dy W_hat;
 * ``linear_transposed_factored``: dx = s2 * (V (g * (U^T (s1 * dy)))).
 
+Format variants (same article, section "Kontext: co existuje kolem"): DBF
+factors a weight into two binary matrices with diagonal scaling, so every
+rank component carries the same magnitude profile; that is the form above
+(the profile s1 s2^T, weighted by g).  MDBF replaces that single profile by
+an envelope of rank l.  Plainest reading: the sign product U diag(g) V^T is
+modulated element by element by E = sum_l s1^(l) s2^(l)^T, i.e.
+
+    W_hat = sum_l diag(s1^(l)) . U . diag(g) . V^T . diag(s2^(l)),
+
+with l pairs of scale vectors sharing U, V and g (``reconstruct_weight_envelope``,
+``linear_envelope_dense``, ``linear_envelope_factored``); l = 1 is the form above.
+
 Storage (same article and section, plus section 'Co znamena "sub-1-bit"'):
 a rank-r factorisation of an m x n matrix stores r(m+n) sign bits; the scale
 parameters counted here are the m + n + r entries of s1, g, s2 at
@@ -104,6 +116,35 @@ def linear_transposed_factored(dy, U, V, s1, g, s2) -> np.ndarray:
     t = t * _f64(g)[None, :]                     # g * t
     z = t @ _f64(V).T                            # V t'              (B x n)
     return z * _f64(s2)[None, :]                 # s2 * z
+
+
+def reconstruct_weight_envelope(U, V, S1, g, S2) -> np.ndarray:
+    """W_hat = sum_l diag(S1[l]) U diag(g) V^T diag(S2[l]); S1 is (l, m), S2 (l, n)."""
+    S1 = np.atleast_2d(_f64(S1))
+    S2 = np.atleast_2d(_f64(S2))
+    if S1.shape[0] != S2.shape[0]:
+        raise ValueError("S1 and S2 must hold the same number of envelope terms")
+    W = np.zeros((S1.shape[1], S2.shape[1]))
+    for a, b in zip(S1, S2):
+        W += reconstruct_weight(U, V, a, g, b)
+    return W
+
+
+def linear_envelope_dense(x, U, V, S1, g, S2) -> np.ndarray:
+    """y = x W_hat^T for the rank-l envelope form, W_hat formed densely."""
+    return _f64(x) @ reconstruct_weight_envelope(U, V, S1, g, S2).T
+
+
+def linear_envelope_factored(x, U, V, S1, g, S2) -> np.ndarray:
+    """y = sum_l S1[l] * (U (g * (V^T (S2[l] * x)))), in fp64."""
+    S1 = np.atleast_2d(_f64(S1))
+    S2 = np.atleast_2d(_f64(S2))
+    if S1.shape[0] != S2.shape[0]:
+        raise ValueError("S1 and S2 must hold the same number of envelope terms")
+    y = np.zeros((np.atleast_2d(x).shape[0], S1.shape[1]))
+    for a, b in zip(S1, S2):
+        y += linear_factored(x, U, V, a, g, b)
+    return y
 
 
 def bits_per_weight(m: int, n: int, r: int, scale_bits: int = 16) -> float:

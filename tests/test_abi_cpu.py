@@ -224,3 +224,21 @@ def test_transpose_validation(L):
     assert t(src, _layer(m=96, n=64, r=40, dt=nq.NQ_F32, blob=FAKE + (1 << 30))) == nq.NQ_ERR_INVALID_ARG
     assert t(src, _layer(m=96, n=64, r=40, blob=FAKE + 256)) == nq.NQ_ERR_INVALID_ARG  # blobs overlap
     assert b"overlap" in L.nq_last_error()
+
+
+def test_envelope_validation(L):
+    lay = _layer(m=64, n=96, r=40)
+    ws = L.nq_workspace_bytes_envelope(ctypes.byref(lay), 2, 1)
+    assert ws > 0
+    assert L.nq_workspace_bytes_envelope(ctypes.byref(lay), 2, 3) == 0  # 6 batch rows: not this path
+    assert L.nq_workspace_bytes_envelope(ctypes.byref(lay), 0, 1) == 0
+    S1, S2, X, Y, W = FAKE + (3 << 30), FAKE + (4 << 30), FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    run = lambda env=2, B=1, s1=S1, s2=S2, wsb=ws: L.nq_linear_fwd_envelope(
+        ctypes.byref(lay), env, s1, s2, X, nq.NQ_BF16, Y, nq.NQ_BF16, B, W, wsb, None)
+    assert run(env=0) == nq.NQ_ERR_INVALID_ARG
+    assert run(env=nq.NQ_ENVELOPE_MAX + 1) == nq.NQ_ERR_INVALID_ARG
+    assert run(s1=0) == nq.NQ_ERR_INVALID_ARG
+    assert run(s2=S2 + 1) == nq.NQ_ERR_INVALID_ARG  # misaligned fp16 array
+    assert run(B=3) == nq.NQ_ERR_UNSUPPORTED
+    assert run(wsb=ws - 1) == nq.NQ_ERR_WORKSPACE
+    assert run(B=0) == nq.NQ_OK
