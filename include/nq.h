@@ -2,10 +2,10 @@
  * nq.h -- C ABI of libnq: linear layers whose weight is a low-rank product of
  * bit-packed sign matrices and diagonal scales, on AMD Instinct MI355X (gfx950).
  *
- * The operation (NanoQuant pages: hardwired.dev article, section "Jak NanoQuant
- * funguje" -- the weight matrix is approximated by a product of binary matrices
- * holding only +1 and -1 and of diagonal scaling vectors; rapidrecap.app
- * summary, "Quantization Technique" -- the binary matrices are called U and V):
+ * The operation (hardwired.dev NanoQuant article, section "Jak NanoQuant
+ * funguje": the weight is factored into sign matrices and diagonal scales;
+ * rapidrecap.app summary, "Quantization Technique": the sign factors are named
+ * U and V), with one diagonal on each side of each sign factor:
  *
  *     W_hat = diag(s1) . U . diag(g) . V^T . diag(s2)        (m x n)
  *     U in {-1,+1}^(m x r),  V in {-1,+1}^(n x r),  s1: m,  g: r,  s2: n
@@ -77,17 +77,17 @@ typedef void* nq_stream_t; /* hipStream_t */
 int32_t nq_abi_version(void);
 
 /* Bytes of device memory a packed layer occupies; 0 for invalid arguments.
- * Storage is r(m+n) sign bits (padded to whole tiles) plus the m+n+r scales
- * (hardwired.dev article, section "Jak NanoQuant funguje": r x (m+n) binary
- * values plus the scaling parameters). */
+ * Storage: the r(m+n) sign bits of U and V (padded to whole tiles) and the
+ * m+n+r scales (storage rule of hardwired.dev, section "Jak NanoQuant
+ * funguje"), plus the header and section alignment. */
 size_t nq_layer_bytes(int32_t m, int32_t n, int32_t r, int32_t scale_dtype);
 
 /* Packs sign matrices and scales into L->blob.
  *   U  : device, m x r int8, row-major, every entry exactly +1 or -1
  *   V  : device, n x r int8, row-major, every entry exactly +1 or -1
  *   s1 : device, m values; g : device, r values; s2 : device, n values (L->scale_dtype)
- * The pages allow only +1 and -1 in the binary factors (hardwired.dev, section
- * "Jak NanoQuant funguje"); any other value, 0 included, makes the call return
+ * The sign factors hold signs only (hardwired.dev, section "Jak NanoQuant
+ * funguje"); any other value, 0 included, makes the call return
  * NQ_ERR_NOT_PM1 (the blob is then unusable).  BLOCKING: synchronises `stream`
  * to read the validation result.  The scales are copied, so the inputs may be
  * freed afterwards. */
@@ -109,8 +109,10 @@ size_t nq_workspace_bytes(const nq_layer* L, int32_t B);
 size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path);
 
 /* y = x W_hat^T for a batch of B rows.
- *   x : device, B x n row-major, x_dtype NQ_BF16 or NQ_F32, 4-byte aligned
- *   y : device, B x m row-major, y_dtype NQ_BF16 or NQ_F32, 4-byte aligned; must not overlap x
+ *   x : device, B x n row-major, x_dtype NQ_BF16 or NQ_F32, aligned to its element size
+ *       (rows that are not 16-byte aligned cost one extra copy launch)
+ *   y : device, B x m row-major, y_dtype NQ_BF16 or NQ_F32, aligned to its element size;
+ *       must not overlap x
  *   workspace : device, >= nq_workspace_bytes(L, B), 256-byte aligned
  * ASYNCHRONOUS: returns once the kernels are enqueued on `stream`; launch errors
  * are returned, faults surface at the caller's next synchronisation.  B == 0
