@@ -342,6 +342,25 @@ def time_graph(torch, stream, step, warmup, steps):
     return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
 
+def read_probe(dev, gib=4, reps=5):
+    """Achievable HBM read rate: torch's sum over `gib` GiB of fp32 (one read
+    of every byte, a tiny write), best of `reps`, timed with events."""
+    import torch
+    x = torch.ones(gib << 28, dtype=torch.float32, device=dev)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None or t < best else best
+    del x
+    torch.cuda.empty_cache()
+    return {"gbs": round((gib << 30) / best / 1e9, 1), "how": f"torch sum over {gib} GiB fp32, best of {reps}"}
+
+
 MFMA_PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 
 
@@ -528,6 +547,8 @@ def run_decode70b(args):
     if not args.no_prefill:
         del layers, xs, ys, ws
         torch.cuda.empty_cache()
+        out["read_probe"] = read_probe(dev)
+        log(f"[bench] read probe: {out['read_probe']['gbs']} GB/s ({out['read_probe']['how']})")
         out["prefill"] = run_prefill70b(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline ...")
