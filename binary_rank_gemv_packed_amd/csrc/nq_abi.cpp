@@ -36,6 +36,7 @@ nq_status ok() {
 constexpr int32_t MAX_DIM = 1 << 20;
 constexpr int32_t MAX_RANK = 1 << 16;
 constexpr int32_t MAX_BATCH = 1 << 20;
+constexpr int32_t DEC_MAX_BATCH = 16;  // the decode path runs B > 4 as chunks of at most 4 rows
 
 int scale_bytes(int32_t dt) { return dt == NQ_F32 ? 4 : (dt == NQ_F16 ? 2 : 0); }
 int act_bytes(int32_t dt) { return dt == NQ_F32 ? 4 : (dt == NQ_BF16 ? 2 : 0); }
@@ -59,14 +60,30 @@ nq_status hip_fail(hipError_t e, const char* what) {
   return fail(NQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Batch rows per launch pair of the decode path for a batch of B <= 16: the
+// largest of min(B, 4) .. 1 whose plan fits (0: none).  Larger batches run as
+// consecutive chunks of that many rows, each reading the weights again.
+int dec_chunk(const nq_layer* L, int32_t B) {
+  if (B < 1 || B > DEC_MAX_BATCH) return 0;
+  for (int c = B < 4 ? B : 4; c >= 1; c--)
+    if (nq::dec_plan(L->m, L->n, L->r, c, scale_bytes(L->scale_dtype)).ok) return c;
+  return 0;
+}
+
 size_t plan_bytes(const nq_layer* L, int32_t B, int32_t path) {
   switch (path) {
     case NQ_PATH_GEMV: return nq::gemv_plan(L->m, L->n, L->r, B).bytes;
     case NQ_PATH_VALU: return nq::valu_plan(L->m, L->n, L->r).bytes;
     case NQ_PATH_GEMM: return nq::gemm_plan(L->m, L->n, L->r, B).bytes;
     case NQ_PATH_DECODE: {
-      nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype));
-      return p.ok ? p.bytes : 0;
+      const int c = dec_chunk(L, B);
+      if (!c) return 0;
+      size_t need = nq::dec_plan(L->m, L->n, L->r, c, scale_bytes(L->scale_dtype)).bytes;
+      if (B % c) {
+        const size_t t = nq::dec_plan(L->m, L->n, L->r, B % c, scale_bytes(L->scale_dtype)).bytes;
+        need = t > need ? t : need;
+      }
+      return need;
     }
   }
   return 0;
@@ -222,13 +239,13 @@ size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path) {
   if (path == NQ_PATH_AUTO) return nq_workspace_bytes(L, B);
   if (path == NQ_PATH_GEMV && B > 16) return 0;
   if (path == NQ_PATH_VALU && B != 1) return 0;
-  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype)).ok) return 0;
+  if (path == NQ_PATH_DECODE && !dec_chunk(L, B)) return 0;
   if (path < NQ_PATH_AUTO || path > NQ_PATH_DECODE) return 0;
   return plan_bytes(L, B, path);
 }
 
 static int32_t auto_path(const nq_layer* L, int32_t B) {
-  if (B <= 4 && nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype)).ok) return NQ_PATH_DECODE;
+  if (B <= DEC_MAX_BATCH && dec_chunk(L, B)) return NQ_PATH_DECODE;
   return B <= 16 ? NQ_PATH_GEMV : NQ_PATH_GEMM;
 }
 
@@ -262,9 +279,9 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   if (path == NQ_PATH_AUTO) path = auto_path(L, B);
   if (path == NQ_PATH_GEMV && B > 16) return fail(NQ_ERR_UNSUPPORTED, "gemv path takes B <= 16 (got %d)", B);
   if (path == NQ_PATH_VALU && B != 1) return fail(NQ_ERR_UNSUPPORTED, "valu path takes B == 1 (got %d)", B);
-  if (path == NQ_PATH_DECODE && !nq::dec_plan(L->m, L->n, L->r, B, scale_bytes(L->scale_dtype)).ok)
-    return fail(NQ_ERR_UNSUPPORTED, "decode path takes B <= 4 and a rank whose image fits in LDS (B=%d r=%d)", B,
-                L->r);
+  if (path == NQ_PATH_DECODE && !dec_chunk(L, B))
+    return fail(NQ_ERR_UNSUPPORTED, "decode path takes B <= %d and a rank whose image fits in LDS (B=%d r=%d)",
+                DEC_MAX_BATCH, B, L->r);
   const size_t need = plan_bytes(L, B, path);
   if (workspace_bytes < need)
     return fail(NQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
@@ -293,7 +310,18 @@ static nq_status fwd_impl(const nq_layer* L, const void* x, int32_t x_dtype, voi
   switch (path) {
     case NQ_PATH_GEMV: e = nq::gemv_forward(a, nq::gemv_plan(a.m, a.n, a.r, B)); break;
     case NQ_PATH_VALU: e = nq::valu_forward(a, nq::valu_plan(a.m, a.n, a.r)); break;
-    case NQ_PATH_DECODE: e = nq::dec_forward(a, nq::dec_plan(a.m, a.n, a.r, B, scale_bytes(a.scale_dtype))); break;
+    case NQ_PATH_DECODE: {  // chunks of dec_chunk rows, one after another on the stream
+      const int c = dec_chunk(L, B);
+      e = hipSuccess;
+      for (int b0 = 0; b0 < B && e == hipSuccess; b0 += c) {
+        nq::FwdArgs ac = a;
+        ac.B = B - b0 < c ? B - b0 : c;
+        ac.x = static_cast<const uint8_t*>(x) + (size_t)b0 * L->n * xb;
+        ac.y = static_cast<uint8_t*>(y) + (size_t)b0 * L->m * yb;
+        e = nq::dec_forward(ac, nq::dec_plan(a.m, a.n, a.r, ac.B, scale_bytes(a.scale_dtype)));
+      }
+      break;
+    }
     default: e = nq::gemm_forward(a, nq::gemm_plan(a.m, a.n, a.r, B)); break;
   }
   if (e != hipSuccess) return hip_fail(e, "forward launch");

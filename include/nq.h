@@ -57,8 +57,9 @@ typedef enum {
   NQ_PATH_GEMM = 2,   /* any B (auto for B > 16, prefill): +-1 signs unpacked to fp16 in LDS,
                          fp16 MFMA with per-row power-of-two activation scales, fp32 accumulate */
   NQ_PATH_VALU = 3,   /* B == 1 only: plain per-bit masked sums on the vector ALU (comparison) */
-  NQ_PATH_DECODE = 4  /* 1 <= B <= 4: the decode path, activation images staged in LDS
-                         (3 launches, 4 when the stage-1 partials are too many to fold)      */
+  NQ_PATH_DECODE = 4  /* 1 <= B <= 16: the decode path, activation images staged in LDS
+                         (2 launches per chunk of <= 4 batch rows, 3 when the stage-1
+                         partials are too many to fold; B > 4 runs as consecutive chunks) */
 } nq_path;
 
 /* A packed layer.  `blob` is device memory of nq_layer_bytes(m, n, r, scale_dtype)
@@ -118,7 +119,7 @@ size_t nq_workspace_bytes_path(const nq_layer* L, int32_t B, int32_t path);
  * are returned, faults surface at the caller's next synchronisation.  B == 0
  * returns NQ_OK and launches nothing.  Stateless and re-entrant; the call
  * sequence may be captured into a HIP graph.  Path chosen automatically:
- * NQ_PATH_DECODE for B <= 4 when its plan fits, NQ_PATH_GEMV for B <= 16,
+ * NQ_PATH_DECODE for B <= 16 when its plan fits, else NQ_PATH_GEMV for B <= 16,
  * NQ_PATH_GEMM above. */
 nq_status nq_linear_fwd(const nq_layer* L, const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
                         int32_t B, void* workspace, size_t workspace_bytes, nq_stream_t stream);

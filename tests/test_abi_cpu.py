@@ -113,7 +113,7 @@ def test_fwd_validation_errors(L):
     assert fwd(L, _layer(), ws=FAKE + (2 << 30) + 128) == E.NQ_ERR_INVALID_ARG
     assert fwd(L, _layer(), B=17, path=nq.PATHS["gemv"]) == E.NQ_ERR_UNSUPPORTED
     assert fwd(L, _layer(), B=2, path=nq.PATHS["valu"]) == E.NQ_ERR_UNSUPPORTED
-    assert fwd(L, _layer(), B=5, path=nq.PATHS["decode"]) == E.NQ_ERR_UNSUPPORTED
+    assert fwd(L, _layer(), B=17, path=nq.PATHS["decode"]) == E.NQ_ERR_UNSUPPORTED
     assert fwd(L, _layer(), B=17, wsb=16) == E.NQ_ERR_WORKSPACE   # B > 16: the prefill path's workspace
     assert b"overlap" not in L.nq_last_error()
     fwd(L, _layer(), y=FAKE + 64)
@@ -147,7 +147,9 @@ def test_workspace_bytes(L):
         need = L.nq_workspace_bytes_path(ref, 1, nq.PATHS[name])
         assert 0 < need <= w1
         assert fwd(L, lay, wsb=need - 1, path=nq.PATHS[name]) == nq.NQ_ERR_WORKSPACE
-    assert L.nq_workspace_bytes_path(ref, 5, nq.PATHS["decode"]) == 0
+    assert L.nq_workspace_bytes_path(ref, 17, nq.PATHS["decode"]) == 0
+    # B = 5..16 runs as chunks of 4 rows: the workspace of one chunk
+    assert L.nq_workspace_bytes_path(ref, 16, nq.PATHS["decode"]) == L.nq_workspace_bytes_path(ref, 4, nq.PATHS["decode"])
     assert L.nq_workspace_bytes_path(ref, 17, nq.PATHS["gemv"]) == 0
     assert L.nq_workspace_bytes_path(ref, 2, nq.PATHS["valu"]) == 0
     assert L.nq_workspace_bytes_path(ref, 1, 99) == 0

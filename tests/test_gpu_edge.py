@@ -73,7 +73,7 @@ def test_path_batch_limits():
     layer = G.pack_layer(L)
     x = G.x_tensor(L.x, L.x_dtype)
     with pytest.raises(nq.NQError) as e:
-        nq.linear(x[:5], layer, path="decode")
+        nq.linear(x, layer, path="decode")  # 17 rows: beyond the chunked decode path
     assert e.value.status == nq.NQ_ERR_UNSUPPORTED
     with pytest.raises(nq.NQError) as e:
         nq.linear(x, layer, path="gemv")

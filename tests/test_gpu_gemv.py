@@ -53,7 +53,7 @@ SMALL = [(256, 256, 64), (63, 17, 5), (100, 300, 130), (1, 1, 1), (16, 128, 128)
          (300, 520, 511)]
 
 
-PATH_B = [("decode", B) for B in (1, 2, 3, 4)] + [("gemv", B) for B in (1, 2, 3, 4, 5, 8, 13, 16)]
+PATH_B = [("decode", B) for B in (1, 2, 3, 4, 5, 8, 13, 16)] + [("gemv", B) for B in (1, 2, 3, 4, 5, 8, 13, 16)]
 
 
 @pytest.mark.parametrize("m,n,r", SMALL)
