@@ -77,6 +77,7 @@ def hip_runtime():
             if "libamdhip64.so" in line:
                 lib = ctypes.CDLL(line.split()[-1])
                 lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+                lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
                 lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
                 lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
                 lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -86,12 +87,16 @@ def hip_runtime():
 
 
 class Events:
-    def __init__(self, hip, n):
+    # hipEventDisableSystemFence: an event only for timing, recorded without the
+    # system-scope cache write-back and invalidate that would slow the next kernel
+    TIMING_ONLY = 0x20000000
+
+    def __init__(self, hip, n, flags=0):
         self.hip = hip
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            assert hip.hipEventCreateWithFlags(ctypes.byref(h), flags) == 0
             self.ev.append(h.value)
 
     def ms(self, i, j):
@@ -271,7 +276,7 @@ def kernel_durations(nq, stream, units, layers, xs, ys, ws, path, hold_cycles=10
     import torch
     hip = hip_runtime()
     EV = 4
-    ev = Events(hip, EV * len(units) + 1)
+    ev = Events(hip, EV * len(units) + 1, Events.TIMING_ONLY)
     lib = nq.lib()
     st = stream.cuda_stream
     pth = nq.PATHS[path]

@@ -355,7 +355,7 @@ static EnvLayout env_layout(const nq_layer* L, int32_t env, size_t fwd_bytes) {
 }
 
 static nq::DecPlan env_plan(const nq_layer* L, int32_t env, int32_t B) {
-  nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B * env, scale_bytes(L->scale_dtype));
+  nq::DecPlan p = nq::dec_plan(L->m, L->n, L->r, B * env, scale_bytes(L->scale_dtype), true);
   if (!p.rows2) p.ok = false;  // the envelope sum lives in the row-split stage 2
   return p;
 }

@@ -42,6 +42,7 @@ constexpr int DEC_MAX_B = 4;           // batch rows of the decode path (4 piece
 constexpr int TARGET_WG = 256;          // one workgroup per CU of an MI355X
 constexpr int MIN_WG = 128;             // fewest workgroups a stage is cut into (half the CUs)
 constexpr int WAVE_BUDGET = 256 * 12;   // resident waves of the chip at <= 168 VGPRs (3 per SIMD)
+constexpr int MIN_ROW_WAVES = 256;      // fewest waves a row-split stage 2 may have
 constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles
 constexpr size_t LDS_S1 = 64 * 1024;    // image bytes a stage-1 workgroup may stage
 constexpr size_t LDS_S2 = 64 * 1024;    // image (+ reduction) bytes of a stage-2 workgroup
@@ -913,14 +914,17 @@ static bool pick_shape(int RT, int splits, int quads, int minwg, int* RM, int* K
 
 // Stage 2 with row-split waves (see s2_rows_body) when every row tile's quads
 // fit one wave's 16-quad buffer: RM row tiles per wave, W waves per workgroup.
-// W is sized so that about 160 workgroups cover the rows and so that the
-// prologue (2 chunks per thread per pass) takes one pass; more than 8 waves
+// Only for stages of at least MIN_ROW_WAVES row tiles, with RM small enough
+// to give that many waves.  W is sized so that about 160 workgroups cover the
+// rows and so that the prologue (2 chunks per thread per pass) takes one pass;
+// more than 8 waves
 // only where the kernel fits 128 VGPRs (RM <= 2, S1 <= 2 partials, B = 1,
 // 2-byte scales).
-static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_bytes, int* RM, int* W) {
-  if (quads > 16) return false;
+static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_bytes, int min_waves, int* RM,
+                      int* W) {
+  if (quads > 16 || RT < min_waves) return false;  // few rows: the K-split keeps more waves busy
   int rm = 8;
-  while (rm > 1 && rm * quads > 16) rm /= 2;
+  while (rm > 1 && (rm * quads > 16 || RT / rm < min_waves)) rm /= 2;
   int w = ceil_div(RT, rm * 160);
   const int w_pass = ceil_div(chunks, 2 * 64);
   w = w > w_pass ? w : w_pass;
@@ -931,7 +935,7 @@ static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_by
   return true;
 }
 
-DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes) {
+DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows) {
   DecPlan p{};
   p.ok = false;
   if (B < 1 || B > DEC_MAX_B) return p;
@@ -1003,7 +1007,7 @@ DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes) {
   p.rows2 = false;
   {
     int rm, w;
-    if (p.fused_mid && pick_rows(p.RT2, quads2, B * p.KT2 * 16, p.S1, B, scale_bytes, &rm, &w) && p.KT2 * tb <= LDS_S2) {
+    if (p.fused_mid && pick_rows(p.RT2, quads2, B * p.KT2 * 16, p.S1, B, scale_bytes, force_rows ? 1 : MIN_ROW_WAVES, &rm, &w) && p.KT2 * tb <= LDS_S2) {
       p.rows2 = true;
       p.RG2 = rm;
       p.KS2 = w;
@@ -1228,7 +1232,7 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_
   p.rows2 = false;
   {
     int rm, w;
-    if (pick_rows(rt2_sum, quads2, B * kt2max * 16, p.S1, B, scale_bytes, &rm, &w)) {
+    if (pick_rows(rt2_sum, quads2, B * kt2max * 16, p.S1, B, scale_bytes, MIN_ROW_WAVES, &rm, &w)) {
       p.rows2 = true;
       p.RG2 = rm;
       p.KS2 = w;

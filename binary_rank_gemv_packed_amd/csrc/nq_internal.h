@@ -92,7 +92,8 @@ struct DecPlan {
   size_t off_img1, off_part, off_img2, off_xpad;
   size_t bytes;
 };
-DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes);  // scale_bytes: 2 (fp16) or 4
+// scale_bytes: 2 (fp16) or 4; force_rows: row-split stage 2 whenever it fits (the envelope needs it)
+DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows = false);
 hipError_t dec_forward(const FwdArgs& a, const DecPlan& p);
 
 // Several layers that share x (same n, scale dtype, batch <= 4) in two

@@ -57,7 +57,9 @@ def test_envelope_fp32_scales_and_inputs():
 
 @pytest.mark.parametrize("B", [1, 2, 4])
 def test_single_term_equals_decode_path_bit_for_bit(B):
-    L, S1, S2 = _env_case(1000, 1100, 600, B, 1, cfg=62)
+    """4096 outputs: tall enough that the plain decode path also uses the
+    row-split stage 2 the envelope runs on, so the two plans coincide."""
+    L, S1, S2 = _env_case(4096, 1100, 600, B, 1, cfg=62)
     layer = G.pack_layer(L)
     assert np.array_equal(_run(L, layer, S1, S2, torch.float32), G.run(L, layer, y_dtype=torch.float32,
                                                                         path="decode"))
