@@ -347,23 +347,48 @@ def time_graph(torch, stream, step, warmup, steps):
     return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
 
-def read_probe(dev, gib=4, reps=5):
-    """Achievable HBM read rate: torch's sum over `gib` GiB of fp32 (one read
-    of every byte, a tiny write), best of `reps`, timed with events."""
+def read_probe(dev, one_shot_bytes, gib=4, reps=5, launches=48, hold_cycles=50_000_000):
+    """Achievable HBM read rates from the library's read probe (sixteen 1 KiB
+    loads in flight per wave, as in the decode kernels' weight stream):
+    `stream` reads `gib` GiB in one launch (best of `reps`); `one_shot` reads
+    `one_shot_bytes` (rounded up to 16 KiB) per launch, `launches` launches back
+    to back on a held stream, each from another region of a buffer far larger
+    than the caches, timed like the decode kernels (event interval per
+    launch, dispatch gap included)."""
     import torch
-    x = torch.ones(gib << 28, dtype=torch.float32, device=dev)
+    import binary_rank_gemv_packed_amd as nq
+    stream = torch.cuda.Stream(device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    buf = torch.ones(gib << 28, dtype=torch.int32, device=dev)
     best = None
-    for _ in range(reps):
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            nq.read_probe(buf, sink, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None or t < best else best
+    out = {"stream": {"bytes": gib << 30, "gbs": round((gib << 30) / best / 1e9, 1)}}
+    words = -(-one_shot_bytes // 16384) * 4096  # int32 words per region
+    regions = buf.numel() // words
+    with torch.cuda.stream(stream):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        x.sum()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3
-        best = t if best is None or t < best else best
-    del x
+        torch.cuda._sleep(hold_cycles)
+        e0.record(stream)
+        for k in range(launches):
+            r = k % regions
+            grid = nq.read_probe(buf[r * words:(r + 1) * words], sink, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    out["one_shot"] = {"bytes": words * 4, "us": round(us, 3), "gbs": round(words * 4 / us / 1e3, 1),
+                       "launch": {"workgroups": grid[0], "threads": grid[1]}, "regions": int(regions)}
+    out["how"] = "nq_read_probe: 16 x 1 KiB loads in flight per wave, XOR of the words"
+    del buf
     torch.cuda.empty_cache()
-    return {"gbs": round((gib << 30) / best / 1e9, 1), "how": f"torch sum over {gib} GiB fp32, best of {reps}"}
+    return out
 
 
 MFMA_PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
@@ -552,8 +577,11 @@ def run_decode70b(args):
     if not args.no_prefill:
         del layers, xs, ys, ws
         torch.cuda.empty_cache()
-        out["read_probe"] = read_probe(dev)
-        log(f"[bench] read probe: {out['read_probe']['gbs']} GB/s ({out['read_probe']['how']})")
+        one = roof["alg_bytes_per_launch"] if roof is not None else 36 << 20
+        rp = out["read_probe"] = read_probe(dev, one)
+        log(f"[bench] read probe: {rp['stream']['gbs']} GB/s over {rp['stream']['bytes'] >> 30} GiB; "
+            f"{rp['one_shot']['bytes'] / 1e6:.2f} MB per launch: {rp['one_shot']['us']} us, "
+            f"{rp['one_shot']['gbs']} GB/s ({rp['one_shot']['launch']['workgroups']} workgroups)")
         out["prefill"] = run_prefill70b(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline ...")

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         "nq_linear_fwd_group": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp]),
         "nq_linear_fwd_group_profiled": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp, vp, c_int,
                                                  ctypes.POINTER(c_int), vp]),
+        "nq_read_probe": (c_int, [vp, c_size, vp, vp, ctypes.POINTER(c_int)]),
         "nq_bits_per_weight": (ctypes.c_double, [c_int, c_int, c_int, c_int]),
         "nq_rank_for_bits": (c_int, [c_int, c_int, ctypes.c_double, c_int]),
         "nq_status_string": (ctypes.c_char_p, [c_int]),
@@ -305,6 +306,18 @@ def linear(x: torch.Tensor, layer: Layer, out_dtype: torch.dtype | None = None, 
         workspace = new_workspace(layer, B)
     linear_into(x2, layer, y, workspace, path, stream)
     return y[0] if squeeze else y
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> tuple[int, int]:
+    """Reads buf once (a measurement aid; see nq_read_probe) and XORs its
+    32-bit words into sink[0] (int32, on buf's device).  Returns the launch's
+    (workgroups, threads per workgroup)."""
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < 1:
+        raise NQError(NQ_ERR_INVALID_ARG, "buf must be contiguous and sink an int32 tensor")
+    grid = (ctypes.c_int32 * 2)()
+    _check(lib().nq_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream(stream),
+                               grid))
+    return int(grid[0]), int(grid[1])
 
 
 def bits_per_weight(m: int, n: int, r: int, scale_bits: int = 16) -> float:

@@ -600,6 +600,23 @@ nq_status nq_linear_fwd(const nq_layer* L, const void* x, int32_t x_dtype, void*
   return nq_linear_fwd_path(L, x, x_dtype, y, y_dtype, B, workspace, workspace_bytes, stream, NQ_PATH_AUTO);
 }
 
+nq_status nq_read_probe(const void* buf, size_t bytes, uint32_t* sink, nq_stream_t stream, int32_t* grid) {
+  if (!buf || !sink) return fail(NQ_ERR_INVALID_ARG, "buf and sink must be given");
+  if (bytes == 0 || bytes % nq::PROBE_BATCH_BYTES)
+    return fail(NQ_ERR_INVALID_ARG, "bytes (%zu) must be a positive multiple of %zu", bytes, nq::PROBE_BATCH_BYTES);
+  if (reinterpret_cast<uintptr_t>(buf) % 16) return fail(NQ_ERR_INVALID_ARG, "buf is not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(sink) % 4) return fail(NQ_ERR_INVALID_ARG, "sink is not 4-byte aligned");
+  if (spans_overlap(buf, bytes, sink, 4)) return fail(NQ_ERR_INVALID_ARG, "sink lies inside buf");
+  dim3 g;
+  const hipError_t e = nq::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream), &g);
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  if (grid) {
+    grid[0] = (int32_t)g.x;
+    grid[1] = 64 * 4;
+  }
+  return NQ_OK;
+}
+
 double nq_bits_per_weight(int32_t m, int32_t n, int32_t r, int32_t scale_bits) {
   if (m < 1 || n < 1 || r < 0 || scale_bits < 0) return -1.0;
   return ((double)r * ((double)m + n) + (double)scale_bits * ((double)m + n + r)) / ((double)m * n);

@@ -142,4 +142,9 @@ struct GemmPlan {
 GemmPlan gemm_plan(int m, int n, int r, int B);
 hipError_t gemm_forward(const FwdArgs& a, const GemmPlan& p);
 
+// Read-rate probe (nq_probe.hip): reads `bytes` (a multiple of
+// PROBE_BATCH_BYTES) once, XORs the words into *sink; *grid receives the grid.
+constexpr size_t PROBE_BATCH_BYTES = 16384;
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s, dim3* grid);
+
 }  // namespace nq

@@ -224,6 +224,18 @@ double nq_bits_per_weight(int32_t m, int32_t n, int32_t r, int32_t scale_bits);
  * 0 when even r = 1 exceeds bpw; -1 for invalid arguments. */
 int32_t nq_rank_for_bits(int32_t m, int32_t n, double bpw, int32_t scale_bits);
 
+/* Measurement aid, not part of the layer's arithmetic: reads `bytes` of device
+ * memory at `buf` once, with the load pattern of the forward kernels' weight
+ * stream (each wave keeps sixteen 1 KiB loads in flight), and XORs every
+ * 32-bit word into *sink (device memory, which the caller initialises; the
+ * call adds XOR(words) to it).  Timing the call with events gives the read
+ * rate a kernel of that shape reaches for that many bytes.  `bytes` must be a
+ * positive multiple of 16384, `buf` 16-byte aligned, `sink` 4-byte aligned
+ * and outside buf; NQ_ERR_INVALID_ARG otherwise.  If grid is not NULL it
+ * receives the workgroups and threads per workgroup of the launch.
+ * Asynchronous on `stream`. */
+nq_status nq_read_probe(const void* buf, size_t bytes, uint32_t* sink, nq_stream_t stream, int32_t* grid);
+
 /* Static text for a status code. */
 const char* nq_status_string(int32_t status);
 

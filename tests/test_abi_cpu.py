@@ -244,3 +244,16 @@ def test_envelope_validation(L):
     assert run(B=3) == nq.NQ_ERR_UNSUPPORTED
     assert run(wsb=ws - 1) == nq.NQ_ERR_WORKSPACE
     assert run(B=0) == nq.NQ_OK
+
+
+def test_read_probe_validation(L):
+    sink = FAKE + (1 << 30)
+    probe = lambda buf=FAKE, nbytes=16384, s=sink: L.nq_read_probe(buf, nbytes, s, None, None)
+    assert probe(buf=0) == nq.NQ_ERR_INVALID_ARG
+    assert probe(s=0) == nq.NQ_ERR_INVALID_ARG
+    assert probe(nbytes=0) == nq.NQ_ERR_INVALID_ARG
+    assert probe(nbytes=16384 + 16) == nq.NQ_ERR_INVALID_ARG  # not a whole number of 16 KiB batches
+    assert probe(buf=FAKE + 8) == nq.NQ_ERR_INVALID_ARG
+    assert probe(s=sink + 2) == nq.NQ_ERR_INVALID_ARG
+    assert probe(s=FAKE + 4096) == nq.NQ_ERR_INVALID_ARG  # sink inside buf
+    assert b"inside" in L.nq_last_error()
