@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         "nq_linear_fwd_group_profiled": (c_int, [vp, c_int, vp, c_int, vp, c_int, c_int, vp, c_size, vp, vp, c_int,
                                                  ctypes.POINTER(c_int), vp]),
         "nq_read_probe": (c_int, [vp, c_size, vp, vp, ctypes.POINTER(c_int)]),
+        "nq_admm_workspace_bytes": (c_size, [c_int, c_int, c_int]),
+        "nq_admm_factorize": (c_int, [vp, c_int, c_int, c_int, vp, vp, ctypes.c_float, c_int, c_int, vp, vp, vp, vp,
+                                      vp, vp, vp, c_size, vp]),
+        "nq_balance_scales": (c_int, [vp, vp, vp, c_int, c_int, c_int, vp]),
         "nq_bits_per_weight": (ctypes.c_double, [c_int, c_int, c_int, c_int]),
         "nq_rank_for_bits": (c_int, [c_int, c_int, ctypes.c_double, c_int]),
         "nq_status_string": (ctypes.c_char_p, [c_int]),
@@ -318,6 +322,47 @@ def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> tuple[int,
     _check(lib().nq_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream(stream),
                                grid))
     return int(grid[0]), int(grid[1])
+
+
+def admm_factorize(W: torch.Tensor, A0: torch.Tensor, B0: torch.Tensor, rho: float, iters: int,
+                   power_iters: int, with_err: bool = True, stream=None):
+    """Initialiser of the binary factors of a dense fp32 weight W (m x n) from
+    latent factors A0 (m x r), B0 (n x r), all on the GPU (nq_admm_factorize).
+    Returns (U int8 m x r, V int8 n x r, s1, g, s2 fp32, err fp32 [iters + 1]
+    or None)."""
+    m, n = W.shape
+    r = A0.shape[1]
+    if A0.shape != (m, r) or B0.shape != (n, r):
+        raise NQError(NQ_ERR_INVALID_ARG, f"A0 {tuple(A0.shape)} / B0 {tuple(B0.shape)} do not match W {m}x{n}, r={r}")
+    for t in (W, A0, B0):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise NQError(NQ_ERR_INVALID_ARG, "W, A0 and B0 must be contiguous fp32 GPU tensors")
+    dev = W.device
+    need = int(lib().nq_admm_workspace_bytes(m, n, r))
+    if need == 0:
+        raise NQError(NQ_ERR_INVALID_ARG, f"invalid dimensions m={m} n={n} r={r}")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    U = torch.empty(m, r, dtype=torch.int8, device=dev)
+    V = torch.empty(n, r, dtype=torch.int8, device=dev)
+    s1 = torch.empty(m, dtype=torch.float32, device=dev)
+    g = torch.empty(r, dtype=torch.float32, device=dev)
+    s2 = torch.empty(n, dtype=torch.float32, device=dev)
+    err = torch.empty(iters + 1, dtype=torch.float32, device=dev) if with_err else None
+    _check(lib().nq_admm_factorize(W.data_ptr(), m, n, r, A0.data_ptr(), B0.data_ptr(), float(rho), iters,
+                                   power_iters, U.data_ptr(), V.data_ptr(), s1.data_ptr(), g.data_ptr(),
+                                   s2.data_ptr(), err.data_ptr() if err is not None else None, ws.data_ptr(),
+                                   ws.numel(), _stream(stream)))
+    return U, V, s1, g, s2, err
+
+
+def balance_scales(s1: torch.Tensor, g: torch.Tensor, s2: torch.Tensor, stream=None) -> None:
+    """Power-of-two magnitude balancing of fp32 GPU scale vectors, in place
+    (nq_balance_scales)."""
+    for t in (s1, g, s2):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise NQError(NQ_ERR_INVALID_ARG, "s1, g and s2 must be contiguous fp32 GPU tensors")
+    _check(lib().nq_balance_scales(s1.data_ptr(), g.data_ptr(), s2.data_ptr(), s1.numel(), s2.numel(), g.numel(),
+                                   _stream(stream)))
 
 
 def bits_per_weight(m: int, n: int, r: int, scale_bits: int = 16) -> float:

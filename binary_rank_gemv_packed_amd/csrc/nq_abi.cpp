@@ -617,6 +617,43 @@ nq_status nq_read_probe(const void* buf, size_t bytes, uint32_t* sink, nq_stream
   return NQ_OK;
 }
 
+size_t nq_admm_workspace_bytes(int32_t m, int32_t n, int32_t r) {
+  if (!dims_ok(m, n, r) || r > 4096 || r > m || r > n) return 0;
+  return nq::admm_workspace_bytes(m, n, r);
+}
+
+nq_status nq_admm_factorize(const float* W, int32_t m, int32_t n, int32_t r, const float* A0, const float* B0,
+                            float rho, int32_t iters, int32_t power_iters, int8_t* U, int8_t* V, float* s1,
+                            float* g, float* s2, float* err, void* workspace, size_t workspace_bytes,
+                            nq_stream_t stream) {
+  if (!W || !A0 || !B0 || !U || !V || !s1 || !g || !s2 || !workspace)
+    return fail(NQ_ERR_INVALID_ARG, "W, A0, B0, U, V, s1, g, s2 and workspace must be given");
+  if (!dims_ok(m, n, r) || r > 4096 || r > m || r > n)
+    return fail(NQ_ERR_INVALID_ARG, "dimensions out of range: m=%d n=%d r=%d (r <= min(m, n, 4096))", m, n, r);
+  if (!(rho > 0.0f) || !std::isfinite(rho)) return fail(NQ_ERR_INVALID_ARG, "rho must be positive and finite");
+  if (iters < 0 || iters > 10000 || power_iters < 0 || power_iters > 1000)
+    return fail(NQ_ERR_INVALID_ARG, "iters (%d) must be in 0..10000, power_iters (%d) in 0..1000", iters, power_iters);
+  const void* fp[] = {W, A0, B0, s1, g, s2, err};
+  for (const void* p : fp)
+    if (p && reinterpret_cast<uintptr_t>(p) % 4) return fail(NQ_ERR_INVALID_ARG, "fp32 arrays must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(NQ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const size_t need = nq::admm_workspace_bytes(m, n, r);
+  if (workspace_bytes < need) return fail(NQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  nq::AdmmArgs a{W, m, n, r, A0, B0, rho, iters, power_iters, U, V, s1, g, s2, err,
+                 static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream)};
+  const hipError_t e = nq::admm_run(a);
+  if (e != hipSuccess) return hip_fail(e, "initialiser launch");
+  return ok();
+}
+
+nq_status nq_balance_scales(float* s1, float* g, float* s2, int32_t m, int32_t n, int32_t r, nq_stream_t stream) {
+  if (!s1 || !g || !s2) return fail(NQ_ERR_INVALID_ARG, "s1, g and s2 must be given");
+  if (!dims_ok(m, n, r)) return fail(NQ_ERR_INVALID_ARG, "dimensions out of range: m=%d n=%d r=%d", m, n, r);
+  const hipError_t e = nq::launch_balance(s1, g, s2, m, n, r, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "balance launch");
+  return ok();
+}
+
 double nq_bits_per_weight(int32_t m, int32_t n, int32_t r, int32_t scale_bits) {
   if (m < 1 || n < 1 || r < 0 || scale_bits < 0) return -1.0;
   return ((double)r * ((double)m + n) + (double)scale_bits * ((double)m + n + r)) / ((double)m * n);

@@ -1,0 +1,436 @@
+// Initialiser of the binary factorisation (ADMM with a sign projection) and
+// magnitude balancing of the scale vectors.
+//
+// Reading of the hardwired.dev NanoQuant article, section "Trikrokovy
+// pipeline", step 2 and the paragraph after it (ADMM alternating a
+// closed-form least-squares solve for the continuous part with a projection
+// onto the binary set; then power-of-two balancing of the scales).  With an
+// identity Hessian the problem is
+//
+//     minimise ||W - A B^T||_F^2,  A = diag(pA) U diag(qA),  B = diag(pB) V diag(qB)
+//
+// and one ADMM step is
+//
+//     A   <- (W B + rho (ZA - LA)) (B^T B + rho I)^-1
+//     B   <- (W^T A + rho (ZB - LB)) (A^T A + rho I)^-1
+//     ZA  <- proj(A + LA),  ZB <- proj(B + LB),  LA += A - ZA,  LB += B - ZB
+//
+// proj(Y) = diag(p) sign(Y) diag(q), (p, q) the leading singular pair of |Y|
+// by K power steps from the constant vector.  The result is the stored form:
+// U = sign(A + LA), V = sign(B + LB), s1 = pA, g = qA * qB, s2 = pB.
+//
+// Kernels: an fp32 MFMA GEMM (v_mfma_f32_16x16x4f32, 64 x 64 tiles, operand
+// strides as arguments so W and W^T share it) for the four products and the
+// two Gram matrices; the r x r inverse by Gauss-Jordan sweeps (one launch per
+// pivot, every element of the sweep in parallel; the matrix is symmetric
+// positive definite, so no pivoting); the power steps as row and column
+// products of |Y| with deterministic, fixed-order reductions.  Everything is
+// fp32; every reduction order is fixed, so a run is reproducible bit for bit.
+#include "nq_common.h"
+#include "nq_internal.h"
+
+namespace nq {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int GT = 64;   // GEMM block tile (rows and columns)
+constexpr int GK = 16;   // GEMM K step
+constexpr int PAD = 4;   // LDS row padding (floats)
+constexpr int COL_CHUNKS = 64;  // row chunks of the column products of |Y|
+
+// C[i][j] = sum_k A(i, k) B(k, j) + epilogue, A(i, k) = A[i * sai + k * sak],
+// B(k, j) = B[k * sbk + j * sbj].  EPI 0: nothing; 1: + rho (Z - L)[i][j]
+// (Z, L with row stride ldz); 2: + rho on the diagonal.
+struct GemmF32 {
+  const float* A;
+  long long sai, sak;
+  const float* B;
+  long long sbk, sbj;
+  float* C;
+  long long ldc;
+  int M, N, K;
+  const float* Z;
+  const float* L;
+  long long ldz;
+  float rho;
+};
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmF32 g) {
+  __shared__ float As[GK][GT + PAD];  // As[k][i]
+  __shared__ float Bs[GK][GT + PAD];  // Bs[k][j]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const bool a_kfast = g.sak == 1, b_jfast = g.sbj == 1;
+  v4f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < g.K; k0 += GK) {
+#pragma unroll
+    for (int c = 0; c < (GT * GK) / 256; c++) {
+      const int e = tid + 256 * c;
+      // A tile: 64 rows x 16 k, consecutive threads along the contiguous index
+      const int ai = a_kfast ? e / GK : e % GT, ak = a_kfast ? e % GK : e / GT;
+      const int gi = m0 + ai, gk = k0 + ak;
+      As[ak][ai] = (gi < g.M && gk < g.K) ? g.A[(long long)gi * g.sai + (long long)gk * g.sak] : 0.0f;
+      const int bj = b_jfast ? e % GT : e / GK, bk = b_jfast ? e / GT : e % GK;
+      const int gj = n0 + bj, gk2 = k0 + bk;
+      Bs[bk][bj] = (gj < g.N && gk2 < g.K) ? g.B[(long long)gk2 * g.sbk + (long long)gj * g.sbj] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < GK; kk += 4) {
+      const int kr = kk + (lane >> 4);
+      float af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) af[i] = As[kr][wm + 16 * i + (lane & 15)];
+#pragma unroll
+      for (int j = 0; j < 2; j++) bf[j] = Bs[kr][wn + 16 * j + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane holds rows 4 * (lane >> 4) + v of each 16 x 16 tile, column lane & 15
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int row = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
+      if (row >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int col = n0 + wn + 16 * j + (lane & 15);
+        if (col >= g.N) continue;
+        float c = acc[i][j][v];
+        if (EPI == 1) c += g.rho * (g.Z[row * g.ldz + col] - g.L[row * g.ldz + col]);
+        if (EPI == 2 && row == col) c += g.rho;
+        g.C[row * g.ldc + col] = c;
+      }
+    }
+}
+
+// One Gauss-Jordan sweep on pivot k of an r x r matrix: out = sweep_k(in).
+// Applied for k = 0 .. r-1 it turns a symmetric positive definite matrix into
+// its inverse (no pivoting needed: every pivot stays positive).
+__global__ void __launch_bounds__(256) gj_sweep_kernel(const float* __restrict__ in, float* __restrict__ out, int r,
+                                                       int k) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)r * r) return;
+  const int i = (int)(e / r), j = (int)(e % r);
+  const float ip = 1.0f / in[(long long)k * r + k];
+  const float rowk = (j == k ? 1.0f : in[(long long)k * r + j]) * ip;  // out[k][j]
+  float v;
+  if (i == k) {
+    v = rowk;
+  } else {
+    const float f = in[(long long)i * r + k];
+    v = (j == k ? 0.0f : in[e]) - f * rowk;
+  }
+  out[e] = v;
+}
+
+// y = x + z elementwise (the projection input A + L).
+__global__ void __launch_bounds__(256) add_kernel(const float* __restrict__ x, const float* __restrict__ z,
+                                                  float* __restrict__ y, long long n) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) y[e] = x[e] + z[e];
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// p[i] = sum_k |Y[i][k]| q[k]: one wave per row, lanes over k, fixed tree.
+__global__ void __launch_bounds__(256) absmv_rows_kernel(const float* __restrict__ Y, int rows, int r,
+                                                         const float* __restrict__ q, float* __restrict__ p) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole waves leave together
+  const float* y = Y + (long long)row * r;
+  float s = 0.0f;
+  for (int k = lane; k < r; k += 64) s += fabsf(y[k]) * q[k];
+  s = wave_sum(s);
+  if (lane == 0) p[row] = s;
+}
+
+// part[c][k] = sum over row chunk c of |Y[i][k]| p[i] (thread per column).
+__global__ void __launch_bounds__(256) absmv_cols_kernel(const float* __restrict__ Y, int rows, int r,
+                                                         const float* __restrict__ p, float* __restrict__ part) {
+  const int k = blockIdx.x * 256 + threadIdx.x, c = blockIdx.y;
+  if (k >= r) return;
+  const int per = (rows + COL_CHUNKS - 1) / COL_CHUNKS;
+  const int i0 = c * per, i1 = min(rows, i0 + per);
+  float s = 0.0f;
+  for (int i = i0; i < i1; i++) s += fabsf(Y[(long long)i * r + k]) * p[i];
+  part[(long long)c * r + k] = s;
+}
+
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int i = 0; i < nw; i++) t += red[i];
+  return t;
+}
+
+// q[k] = sum_c part[c][k] (when part != null), then v /= ||v|| (if > 0) and
+// *norm_out = ||v||.  One workgroup of 1024 threads.
+__global__ void __launch_bounds__(1024) normalize_kernel(const float* __restrict__ part, float* __restrict__ v, int len,
+                                                         float* __restrict__ norm_out) {
+  __shared__ float red[16];
+  float s = 0.0f;
+  for (int k = threadIdx.x; k < len; k += 1024) {
+    float x;
+    if (part) {
+      x = 0.0f;
+      for (int c = 0; c < COL_CHUNKS; c++) x += part[(long long)c * len + k];
+      v[k] = x;
+    } else {
+      x = v[k];
+    }
+    s += x * x;
+  }
+  // the column sums above are written and re-read by the same thread
+  const float nrm = sqrtf(block_sum(s, red));
+  const float inv = nrm > 0.0f ? 1.0f / nrm : 1.0f;
+  for (int k = threadIdx.x; k < len; k += 1024) v[k] = nrm > 0.0f ? v[k] * inv : v[k];
+  if (threadIdx.x == 0 && norm_out) *norm_out = nrm;
+}
+
+__global__ void __launch_bounds__(256) fill_kernel(float* __restrict__ v, int n, float val) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < n) v[e] = val;
+}
+
+// Z = diag(p) sign(Y) diag(q) * sigma (p, q unit vectors, sigma = ||.||),
+// optional dual update L += X - Z, optional int8 signs.  Also writes the
+// scaled vectors ps = p sqrt(sigma), qs = q sqrt(sigma) (block 0).
+__global__ void __launch_bounds__(256) finish_proj_kernel(const float* __restrict__ Y, int rows, int r,
+                                                          const float* __restrict__ p, const float* __restrict__ q,
+                                                          const float* __restrict__ sigma, float* __restrict__ Z,
+                                                          float* __restrict__ L, const float* __restrict__ X,
+                                                          int8_t* __restrict__ S) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)rows * r) return;
+  const int i = (int)(e / r), k = (int)(e % r);
+  const float root = sqrtf(*sigma);
+  const float y = Y[e];
+  const float sg = y >= 0.0f ? 1.0f : -1.0f;
+  const float z = sg * (p[i] * root) * (q[k] * root);
+  Z[e] = z;
+  if (L) L[e] += X[e] - z;
+  if (S) S[e] = (int8_t)(y >= 0.0f ? 1 : -1);
+}
+
+// ps = p sqrt(sigma) (len values).
+__global__ void __launch_bounds__(256) scale_vec_kernel(const float* __restrict__ p, const float* __restrict__ sigma,
+                                                        float* __restrict__ out, int len, const float* __restrict__ mul) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= len) return;
+  float v = p[e] * sqrtf(*sigma);
+  if (mul) v *= mul[e];
+  out[e] = v;
+}
+
+// sum over e of x[e] * y[e] -> *out, one workgroup (fixed order).
+__global__ void __launch_bounds__(1024) dot_kernel(const float* __restrict__ x, const float* __restrict__ y,
+                                                   long long n, float* __restrict__ out) {
+  __shared__ float red[16];
+  float s = 0.0f;
+  for (long long e = threadIdx.x; e < n; e += 1024) s += x[e] * y[e];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) *out = s;
+}
+
+// err = (w2 - 2 cross + gram) / w2 from the three scalars.
+__global__ void err_kernel(const float* __restrict__ sc, float* __restrict__ err) {
+  const float w2 = sc[0], cross = sc[1], gram = sc[2];
+  *err = (w2 - 2.0f * cross + gram) / w2;
+}
+
+// Power-of-two balancing of s1 (m), g (r), s2 (n) in place; one workgroup.
+__device__ float balance_factor(float ss, int len) {
+  const float rms = sqrtf(ss / (float)len);
+  if (!(rms > 0.0f) || !(rms <= 3.4028235e38f)) return 1.0f;
+  const int e = __builtin_amdgcn_frexp_expf(rms);  // rms = f 2^e, f in [0.5, 1)
+  return __builtin_ldexpf(1.0f, 1 - e);
+}
+
+__global__ void __launch_bounds__(1024) balance_kernel(float* __restrict__ s1, float* __restrict__ g,
+                                                       float* __restrict__ s2, int m, int n, int r) {
+  __shared__ float red[16];
+  float a = 0.0f, b = 0.0f;
+  for (int i = threadIdx.x; i < m; i += 1024) a += s1[i] * s1[i];
+  for (int i = threadIdx.x; i < n; i += 1024) b += s2[i] * s2[i];
+  a = block_sum(a, red);
+  b = block_sum(b, red);
+  const float c = balance_factor(a, m), d = balance_factor(b, n);
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += 1024) s1[i] *= c;
+  for (int i = threadIdx.x; i < n; i += 1024) s2[i] *= d;
+  const float gd = 1.0f / (c * d);  // a power of two: exact
+  for (int i = threadIdx.x; i < r; i += 1024) g[i] *= gd;
+}
+
+inline unsigned blocks(long long n, int t) { return (unsigned)((n + t - 1) / t); }
+
+struct AdmmWs {
+  float *A, *B, *ZA, *ZB, *LA, *LB, *T, *G, *Gi;
+  float *pA, *qA, *pB, *qB, *pv, *qv, *part, *sig, *sc;
+};
+
+AdmmWs ws_layout(uint8_t* base, int m, int n, int r, size_t* total) {
+  size_t o = 0;
+  auto take = [&](size_t floats) {
+    size_t at = o;
+    o = align_up(o + floats * 4, 256);
+    return reinterpret_cast<float*>(base + at);
+  };
+  const size_t mr = (size_t)m * r, nr = (size_t)n * r, rr = (size_t)r * r;
+  const int mx = m > n ? m : n;
+  AdmmWs w;
+  w.A = take(mr);
+  w.B = take(nr);
+  w.ZA = take(mr);
+  w.ZB = take(nr);
+  w.LA = take(mr);
+  w.LB = take(nr);
+  w.T = take((size_t)mx * r);
+  w.G = take(rr);
+  w.Gi = take(rr);
+  w.pA = take(m);
+  w.qA = take(r);
+  w.pB = take(n);
+  w.qB = take(r);
+  w.pv = take(mx);
+  w.qv = take(r);
+  w.part = take((size_t)COL_CHUNKS * r);
+  w.sig = take(4);
+  w.sc = take(4);
+  *total = o;
+  return w;
+}
+
+void gemm(hipStream_t st, int epi, const float* A, long long sai, long long sak, const float* B, long long sbk,
+          long long sbj, float* C, long long ldc, int M, int N, int K, const float* Z = nullptr,
+          const float* L = nullptr, long long ldz = 0, float rho = 0.0f) {
+  GemmF32 g{A, sai, sak, B, sbk, sbj, C, ldc, M, N, K, Z, L, ldz, rho};
+  dim3 grid(blocks(N, GT), blocks(M, GT));
+  if (epi == 1) hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, dim3(256), 0, st, g);
+  else if (epi == 2) hipLaunchKernelGGL(gemm_f32_kernel<2>, grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL(gemm_f32_kernel<0>, grid, dim3(256), 0, st, g);
+}
+
+// G (r x r, SPD) -> its inverse in `dst` (G is overwritten: the sweeps
+// alternate between the two buffers and the last one lands in dst).
+void spd_inverse(hipStream_t st, float* G, float* Gi, int r, float** dst) {
+  float* in = G;
+  float* out = Gi;
+  for (int k = 0; k < r; k++) {
+    hipLaunchKernelGGL(gj_sweep_kernel, dim3(blocks((long long)r * r, 256)), dim3(256), 0, st, in, out, r, k);
+    float* t = in;
+    in = out;
+    out = t;
+  }
+  *dst = in;
+}
+
+// proj(Y) of a rows x r matrix: Z, optional dual update with X, optional
+// signs; the scaled singular vectors go to ps (rows) and qs (r).
+void project(hipStream_t st, const AdmmWs& w, const float* Y, int rows, int r, int K, float* Z, float* L,
+             const float* X, int8_t* S, float* ps, float* qs) {
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks(r, 256)), dim3(256), 0, st, w.qv, r, 1.0f / sqrtf((float)r));
+  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, w.sig, 1, 0.0f);
+  for (int it = 0; it < K; it++) {
+    hipLaunchKernelGGL(absmv_rows_kernel, dim3(blocks(rows, 4)), dim3(256), 0, st, Y, rows, r, w.qv, w.pv);
+    hipLaunchKernelGGL(normalize_kernel, dim3(1), dim3(1024), 0, st, nullptr, w.pv, rows, nullptr);
+    hipLaunchKernelGGL(absmv_cols_kernel, dim3(blocks(r, 256), COL_CHUNKS), dim3(256), 0, st, Y, rows, r, w.pv,
+                       w.part);
+    hipLaunchKernelGGL(normalize_kernel, dim3(1), dim3(1024), 0, st, w.part, w.qv, r, w.sig);
+  }
+  if (K == 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks(rows, 256)), dim3(256), 0, st, w.pv, rows, 0.0f);
+  hipLaunchKernelGGL(finish_proj_kernel, dim3(blocks((long long)rows * r, 256)), dim3(256), 0, st, Y, rows, r, w.pv,
+                     w.qv, w.sig, Z, L, X, S);
+  hipLaunchKernelGGL(scale_vec_kernel, dim3(blocks(rows, 256)), dim3(256), 0, st, w.pv, w.sig, ps, rows, nullptr);
+  hipLaunchKernelGGL(scale_vec_kernel, dim3(blocks(r, 256)), dim3(256), 0, st, w.qv, w.sig, qs, r, nullptr);
+}
+
+// err = ||W - ZA ZB^T||^2 / ||W||^2 via W ZB, the Gram matrices and two dots.
+void rel_err(hipStream_t st, const AdmmWs& w, const float* W, int m, int n, int r, float* err) {
+  hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, st, W, W, (long long)m * n, w.sc + 0);
+  gemm(st, 0, W, n, 1, w.ZB, r, 1, w.T, r, m, r, n);                       // W ZB
+  hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, st, w.ZA, w.T, (long long)m * r, w.sc + 1);
+  gemm(st, 0, w.ZA, 1, r, w.ZA, r, 1, w.G, r, r, r, m);                    // ZA^T ZA
+  gemm(st, 0, w.ZB, 1, r, w.ZB, r, 1, w.Gi, r, r, r, n);                   // ZB^T ZB
+  hipLaunchKernelGGL(dot_kernel, dim3(1), dim3(1024), 0, st, w.G, w.Gi, (long long)r * r, w.sc + 2);
+  hipLaunchKernelGGL(err_kernel, dim3(1), dim3(1), 0, st, w.sc, err);
+}
+
+}  // namespace
+
+size_t admm_workspace_bytes(int m, int n, int r) {
+  size_t total = 0;
+  ws_layout(nullptr, m, n, r, &total);
+  return total;
+}
+
+hipError_t admm_run(const AdmmArgs& a) {
+  size_t total = 0;
+  const AdmmWs w = ws_layout(a.ws, a.m, a.n, a.r, &total);
+  const int m = a.m, n = a.n, r = a.r;
+  hipStream_t st = a.stream;
+  const long long mr = (long long)m * r, nr = (long long)n * r;
+  hipMemcpyAsync(w.A, a.A0, mr * 4, hipMemcpyDeviceToDevice, st);
+  hipMemcpyAsync(w.B, a.B0, nr * 4, hipMemcpyDeviceToDevice, st);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks(mr, 256)), dim3(256), 0, st, w.LA, (int)mr, 0.0f);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks(nr, 256)), dim3(256), 0, st, w.LB, (int)nr, 0.0f);
+  const bool last0 = a.iters == 0;
+  project(st, w, w.A, m, r, a.power_iters, w.ZA, nullptr, nullptr, last0 ? a.U : nullptr, w.pA, w.qA);
+  project(st, w, w.B, n, r, a.power_iters, w.ZB, nullptr, nullptr, last0 ? a.V : nullptr, w.pB, w.qB);
+  if (a.err) rel_err(st, w, a.W, m, n, r, a.err);
+  for (int t = 0; t < a.iters; t++) {
+    const bool last = t == a.iters - 1;
+    float* Ginv = nullptr;
+    // A <- (W B + rho (ZA - LA)) (B^T B + rho I)^-1
+    gemm(st, 2, w.B, 1, r, w.B, r, 1, w.G, r, r, r, n, nullptr, nullptr, 0, a.rho);
+    spd_inverse(st, w.G, w.Gi, r, &Ginv);
+    gemm(st, 1, a.W, n, 1, w.B, r, 1, w.T, r, m, r, n, w.ZA, w.LA, r, a.rho);
+    gemm(st, 0, w.T, r, 1, Ginv, r, 1, w.A, r, m, r, r);
+    // B <- (W^T A + rho (ZB - LB)) (A^T A + rho I)^-1
+    gemm(st, 2, w.A, 1, r, w.A, r, 1, w.G, r, r, r, m, nullptr, nullptr, 0, a.rho);
+    spd_inverse(st, w.G, w.Gi, r, &Ginv);
+    gemm(st, 1, a.W, 1, n, w.A, r, 1, w.T, r, n, r, m, w.ZB, w.LB, r, a.rho);
+    gemm(st, 0, w.T, r, 1, Ginv, r, 1, w.B, r, n, r, r);
+    // ZA <- proj(A + LA), LA += A - ZA; the same for B
+    hipLaunchKernelGGL(add_kernel, dim3(blocks(mr, 256)), dim3(256), 0, st, w.A, w.LA, w.T, mr);
+    project(st, w, w.T, m, r, a.power_iters, w.ZA, w.LA, w.A, last ? a.U : nullptr, w.pA, w.qA);
+    hipLaunchKernelGGL(add_kernel, dim3(blocks(nr, 256)), dim3(256), 0, st, w.B, w.LB, w.T, nr);
+    project(st, w, w.T, n, r, a.power_iters, w.ZB, w.LB, w.B, last ? a.V : nullptr, w.pB, w.qB);
+    if (a.err) rel_err(st, w, a.W, m, n, r, a.err + t + 1);
+  }
+  // s1 = pA, g = qA * qB, s2 = pB (the scaled vectors of the last projections)
+  hipMemcpyAsync(a.s1, w.pA, (size_t)m * 4, hipMemcpyDeviceToDevice, st);
+  hipMemcpyAsync(a.s2, w.pB, (size_t)n * 4, hipMemcpyDeviceToDevice, st);
+  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, w.sc + 3, 1, 1.0f);
+  hipLaunchKernelGGL(scale_vec_kernel, dim3(blocks(r, 256)), dim3(256), 0, st, w.qA, w.sc + 3, a.g, r, w.qB);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance(float* s1, float* g, float* s2, int m, int n, int r, hipStream_t st) {
+  hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(1024), 0, st, s1, g, s2, m, n, r);
+  return hipGetLastError();
+}
+
+}  // namespace nq

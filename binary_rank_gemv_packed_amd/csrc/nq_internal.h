@@ -147,4 +147,29 @@ hipError_t gemm_forward(const FwdArgs& a, const GemmPlan& p);
 constexpr size_t PROBE_BATCH_BYTES = 16384;
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s, dim3* grid);
 
+// Initialiser (nq_admm.hip): `iters` ADMM steps with a sign projection from
+// the latent factors A0 (m x r), B0 (n x r) for W (m x n), all fp32 row-major
+// on the device; writes U (m x r), V (n x r) int8 +-1, s1 (m), g (r), s2 (n)
+// fp32 and, when err is not null, iters + 1 relative squared errors.
+struct AdmmArgs {
+  const float* W;
+  int m, n, r;
+  const float* A0;
+  const float* B0;
+  float rho;
+  int iters, power_iters;
+  int8_t* U;
+  int8_t* V;
+  float* s1;
+  float* g;
+  float* s2;
+  float* err;
+  uint8_t* ws;
+  hipStream_t stream;
+};
+size_t admm_workspace_bytes(int m, int n, int r);
+hipError_t admm_run(const AdmmArgs& a);
+hipError_t launch_balance(float* s1, float* g, float* s2, int m, int n, int r, hipStream_t st);
+
 }  // namespace nq
+

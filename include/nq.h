@@ -215,6 +215,43 @@ nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dty
                                  nq_stream_t stream, int32_t path, void* const* events,
                                  int32_t n_events, int32_t* n_launches, int32_t* launch_dims);
 
+/* Initialiser of the factors from a dense weight (hardwired.dev NanoQuant
+ * page, section "Trikrokovy pipeline", step 2 and the paragraph after it:
+ * ADMM that alternates a closed-form least-squares solve of the continuous
+ * part with a projection onto the binary set).  Reading, with an identity
+ * Hessian: minimise ||W - A B^T||_F^2 with A = diag(s1) U diag(qA) and
+ * B = diag(s2) V diag(qB); `iters` ADMM steps of penalty rho from the latent
+ * factors A0, B0:
+ *   A <- (W B + rho (ZA - LA)) (B^T B + rho I)^-1,  B <- (W^T A + rho (ZB - LB)) (A^T A + rho I)^-1,
+ *   ZA <- proj(A + LA), ZB <- proj(B + LB), LA += A - ZA, LB += B - ZB,
+ * proj(Y) = diag(p) sign(Y) diag(q) with (p, q) the leading singular pair of
+ * |Y| from `power_iters` power steps (sign(0) = +1; ZA, ZB start at proj(A0),
+ * proj(B0), the duals at 0).  Outputs (device, caller-owned): U (m x r) and V
+ * (n x r) int8 +-1 row-major, s1 (m), g = qA qB (r), s2 (n) fp32, ready for
+ * nq_pack_factors (after conversion to the scale dtype); if err is not NULL,
+ * err[t] = ||W - W_hat_t||_F^2 / ||W||_F^2 after t steps, t = 0..iters.
+ * Inputs: W (m x n), A0 (m x r), B0 (n x r), device fp32 row-major, 4-byte
+ * aligned, not overlapping the outputs or the workspace.  All arithmetic is
+ * fp32 (MFMA products, Gauss-Jordan inverse of the r x r Gram matrices) with
+ * fixed reduction orders: repeated calls give identical bits.  rho > 0,
+ * 0 <= iters <= 10000, 0 <= power_iters <= 1000, r <= min(m, n, 4096);
+ * NQ_ERR_INVALID_ARG otherwise, NQ_ERR_WORKSPACE for a short workspace.
+ * Asynchronous on `stream`. */
+size_t nq_admm_workspace_bytes(int32_t m, int32_t n, int32_t r);
+nq_status nq_admm_factorize(const float* W, int32_t m, int32_t n, int32_t r, const float* A0, const float* B0,
+                            float rho, int32_t iters, int32_t power_iters, int8_t* U, int8_t* V, float* s1,
+                            float* g, float* s2, float* err, void* workspace, size_t workspace_bytes,
+                            nq_stream_t stream);
+
+/* Magnitude balancing (same page and section, the paragraph after step 2:
+ * the scale factors are evened out so that the binary factors have a balanced
+ * range).  In place on device fp32 s1 (m), g (r), s2 (n): s1 *= c, s2 *= d,
+ * g /= c d with c, d the powers of two that put the root-mean-square of s1
+ * and of s2 in [1, 2) (1 for a zero or non-finite one).  W_hat is unchanged
+ * bit for bit.  NQ_ERR_INVALID_ARG for null pointers or dimensions out of
+ * range.  Asynchronous on `stream`. */
+nq_status nq_balance_scales(float* s1, float* g, float* s2, int32_t m, int32_t n, int32_t r, nq_stream_t stream);
+
 /* Average bits per original weight: (r(m+n) + scale_bits (m+n+r)) / (m n)
  * (hardwired.dev, sections "Jak NanoQuant funguje" and 'Co znamena
  * "sub-1-bit"').  Padding is not counted.  Returns -1.0 for invalid arguments. */

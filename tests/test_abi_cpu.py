@@ -257,3 +257,31 @@ def test_read_probe_validation(L):
     assert probe(s=sink + 2) == nq.NQ_ERR_INVALID_ARG
     assert probe(s=FAKE + 4096) == nq.NQ_ERR_INVALID_ARG  # sink inside buf
     assert b"inside" in L.nq_last_error()
+
+
+def test_admm_validation(L):
+    ws_need = L.nq_admm_workspace_bytes(64, 48, 8)
+    assert ws_need > 0
+    assert L.nq_admm_workspace_bytes(64, 48, 49) == 0  # r > min(m, n)
+    assert L.nq_admm_workspace_bytes(0, 48, 8) == 0
+    P = FAKE
+    args = dict(W=P, m=64, n=48, r=8, A0=P, B0=P, rho=1.0, iters=2, K=3, U=P, V=P, s1=P, g=P, s2=P, err=None,
+                ws=P, wsb=ws_need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.nq_admm_factorize(a["W"], a["m"], a["n"], a["r"], a["A0"], a["B0"], a["rho"], a["iters"], a["K"],
+                                   a["U"], a["V"], a["s1"], a["g"], a["s2"], a["err"], a["ws"], a["wsb"], None)
+    assert call(W=None) == nq.NQ_ERR_INVALID_ARG
+    assert call(s2=None) == nq.NQ_ERR_INVALID_ARG
+    assert call(r=49) == nq.NQ_ERR_INVALID_ARG
+    assert call(rho=0.0) == nq.NQ_ERR_INVALID_ARG
+    assert call(rho=float("nan")) == nq.NQ_ERR_INVALID_ARG
+    assert call(iters=-1) == nq.NQ_ERR_INVALID_ARG
+    assert call(K=1001) == nq.NQ_ERR_INVALID_ARG
+    assert call(W=P + 2) == nq.NQ_ERR_INVALID_ARG
+    assert call(ws=P + 16) == nq.NQ_ERR_INVALID_ARG
+    assert call(wsb=ws_need - 1) == nq.NQ_ERR_WORKSPACE
+    assert b"workspace" in L.nq_last_error()
+    assert L.nq_balance_scales(None, P, P, 4, 4, 2, None) == nq.NQ_ERR_INVALID_ARG
+    assert L.nq_balance_scales(P, P, P, 0, 4, 2, None) == nq.NQ_ERR_INVALID_ARG
