@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="time the 560 linears one by one (no layer groups)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill section")
+    ap.add_argument("--no-initializer", action="store_true", help="skip the ADMM initialiser section")
+    ap.add_argument("--initializer-only", action="store_true", help="run only the ADMM initialiser section")
     ap.add_argument("--suite", default=None, choices=["7b"])
     ap.add_argument("--out", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -583,10 +585,60 @@ def run_decode70b(args):
             f"{rp['one_shot']['bytes'] / 1e6:.2f} MB per launch: {rp['one_shot']['us']} us, "
             f"{rp['one_shot']['gbs']} GB/s ({rp['one_shot']['launch']['workgroups']} workgroups)")
         out["prefill"] = run_prefill70b(dev)
+    if not args.no_initializer:
+        out["initializer"] = run_initializer(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline(spec, B)
     print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------ initialiser (ADMM)
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def run_initializer(dev, m=4096, n=4096, bpw=0.8, power_iters=8, rho=10.0):
+    """ADMM initialiser (nq_admm_factorize) on a Llama-2-7B q-projection shape
+    at 0.8 bits/weight: time per ADMM step = (time of 2 steps - time of 0
+    steps) / 2, HIP events on the launch stream, median of 3.  Flops per step:
+    the four products W B, W^T A, T Ginv (twice) and the two Gram matrices,
+    4 m n r + 4 (m + n) r^2, plus 2 r^3 per Gauss-Jordan inverse (two per
+    step); utilisation against the fp32 matrix peak.  Inputs: W ~ N(0, 1/n)
+    and latent starts ~ N(0, 1), seeded (torch generator)."""
+    import torch
+    import binary_rank_gemv_packed_amd as nq
+    hip = hip_runtime()
+    r = nq.rank_for_bits(m, n, bpw, 16)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260206)
+    W = torch.randn(m, n, generator=gen, device=dev) / (n ** 0.5)
+    A0 = torch.randn(m, r, generator=gen, device=dev)
+    B0 = torch.randn(n, r, generator=gen, device=dev)
+    stream = torch.cuda.Stream()
+    ev = Events(hip, 2)
+
+    def timed(iters):
+        with torch.cuda.stream(stream):
+            hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(stream.cuda_stream))
+            res = nq.admm_factorize(W, A0, B0, rho, iters, power_iters, with_err=False, stream=stream)
+            hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        return ev.ms(0, 1), res
+
+    timed(1)
+    t0 = statistics.median(timed(0)[0] for _ in range(3))
+    t2 = statistics.median(timed(2)[0] for _ in range(3))
+    ev.close()
+    per = (t2 - t0) / 2
+    gemm_flops = 4.0 * m * n * r + 4.0 * (m + n) * r * r
+    inv_flops = 2 * 2.0 * r ** 3
+    tf = (gemm_flops + inv_flops) / (per * 1e-3) / 1e12
+    log(f"[bench] initializer {m}x{n} r={r}: {per:.2f} ms per ADMM step, {tf:.1f} TFLOP/s")
+    return {"workload": f"ADMM initialiser, llama2-7b q-projection shape {m}x{n}, r={r} (0.8 bpw), fp32",
+            "m": m, "n": n, "r": r, "rho": rho, "power_iters": power_iters,
+            "ms_per_step": round(per, 3), "ms_setup_and_projection": round(t0, 3),
+            "flops_per_step": gemm_flops + inv_flops, "tflops": round(tf, 2),
+            "mfma_util_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "peak_tflops": FP32_MFMA_PEAK_TFLOPS}
 
 
 # ------------------------------------------------------------------ 7B per-shape suite
@@ -829,6 +881,8 @@ def main():
         copy_calibration()
     elif args.suite == "7b":
         run_suite7b(args)
+    elif args.initializer_only:
+        print(json.dumps({"initializer": run_initializer("cuda:0")}), flush=True)
     else:
         run_decode70b(args)
 

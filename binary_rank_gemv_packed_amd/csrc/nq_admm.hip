@@ -21,9 +21,9 @@
 //
 // Kernels: an fp32 MFMA GEMM (v_mfma_f32_16x16x4f32, 64 x 64 tiles, operand
 // strides as arguments so W and W^T share it) for the four products and the
-// two Gram matrices; the r x r inverse by Gauss-Jordan sweeps (one launch per
-// pivot, every element of the sweep in parallel; the matrix is symmetric
-// positive definite, so no pivoting); the power steps as row and column
+// two Gram matrices; the r x r inverse by block Gauss-Jordan (64 pivots a
+// step: the pivot block inverted in LDS, then a rank-64 update of the whole
+// matrix; symmetric positive definite, so no pivoting); the power steps as row and column
 // products of |Y| with deterministic, fixed-order reductions.  Everything is
 // fp32; every reduction order is fixed, so a run is reproducible bit for bit.
 #include "nq_common.h"
@@ -117,24 +117,111 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmF32 g) {
     }
 }
 
-// One Gauss-Jordan sweep on pivot k of an r x r matrix: out = sweep_k(in).
-// Applied for k = 0 .. r-1 it turns a symmetric positive definite matrix into
-// its inverse (no pivoting needed: every pivot stays positive).
-__global__ void __launch_bounds__(256) gj_sweep_kernel(const float* __restrict__ in, float* __restrict__ out, int r,
-                                                       int k) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (long long)r * r) return;
-  const int i = (int)(e / r), j = (int)(e % r);
-  const float ip = 1.0f / in[(long long)k * r + k];
-  const float rowk = (j == k ? 1.0f : in[(long long)k * r + j]) * ip;  // out[k][j]
-  float v;
-  if (i == k) {
-    v = rowk;
-  } else {
-    const float f = in[(long long)i * r + k];
-    v = (j == k ? 0.0f : in[e]) - f * rowk;
+// Block Gauss-Jordan inverse of a symmetric positive definite r x r matrix M,
+// in place, one pivot block K = [k0, k0 + bk) (bk <= GJB) per step; every
+// pivot block of an SPD matrix (and of its partial sweeps) is SPD, so no
+// pivoting is needed.  With P = M[K][K], C = M[:][K] and
+// R[t][j] = (P^-1 M[K][:])[t][j] for j outside K, (P^-1)[t][j - k0] inside,
+// one step is
+//     M[i][j] <- R[i - k0][j]                                   i in K
+//     M[i][j] <- (j in K ? 0 : M[i][j]) - sum_t C[i][t] R[t][j]  i outside K
+// (the exchange of the pivot block: after all blocks M holds its inverse).
+constexpr int GJB = 64;
+
+// P^-1 of the bk x bk pivot block by scalar Gauss-Jordan sweeps in LDS (one
+// workgroup of 1024 threads: thread (i, c) holds row i = tid / 16, columns
+// c + 16 u; two buffers so that a sweep reads only the previous one).
+constexpr int GJL = GJB + 1;  // LDS row stride (column reads hit distinct banks)
+__global__ void __launch_bounds__(1024) gj_block_inv_kernel(const float* __restrict__ M, int r, int k0, int bk,
+                                                            float* __restrict__ Pinv) {
+  __shared__ float buf[2][GJB * GJL];
+  const int i = threadIdx.x >> 4, c0 = threadIdx.x & 15;
+#pragma unroll
+  for (int u = 0; u < GJB / 16; u++) {
+    const int j = c0 + 16 * u;
+    buf[0][i * GJL + j] = (i < bk && j < bk) ? M[(long long)(k0 + i) * r + k0 + j] : 0.0f;
   }
-  out[e] = v;
+  __syncthreads();
+  int cur = 0;
+  for (int k = 0; k < bk; k++) {
+    const float* in = buf[cur];
+    float* out = buf[cur ^ 1];
+    const float ip = 1.0f / in[k * GJL + k];
+    const float fi = in[i * GJL + k];
+#pragma unroll
+    for (int u = 0; u < GJB / 16; u++) {
+      const int j = c0 + 16 * u;
+      const float rowk = (j == k ? 1.0f : in[k * GJL + j]) * ip;
+      out[i * GJL + j] = i == k ? rowk : (j == k ? 0.0f : in[i * GJL + j]) - fi * rowk;
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+#pragma unroll
+  for (int u = 0; u < GJB / 16; u++) {
+    const int j = c0 + 16 * u;
+    if (i < bk && j < bk) Pinv[i * bk + j] = buf[cur][i * GJL + j];
+  }
+}
+
+// R (bk x r) and C (r x GJB, first bk columns) of one step from the current M
+// (thread per element R[t][j] and C[j][t], t = blockIdx.y).
+__global__ void __launch_bounds__(256) gj_panel_kernel(const float* __restrict__ M, int r, int k0, int bk,
+                                                       const float* __restrict__ Pinv, float* __restrict__ R,
+                                                       float* __restrict__ C) {
+  const int j = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
+  if (j >= r) return;
+  float v;
+  if (j >= k0 && j < k0 + bk) {
+    v = Pinv[t * bk + (j - k0)];
+  } else {
+    v = 0.0f;
+    for (int u = 0; u < bk; u++) v += Pinv[t * bk + u] * M[(long long)(k0 + u) * r + j];
+  }
+  R[(long long)t * r + j] = v;
+  C[(long long)j * GJB + t] = M[(long long)j * r + k0 + t];
+}
+
+// The rank-bk update of one step, 64 x 64 tiles of M (4 x 4 per thread).
+__global__ void __launch_bounds__(256) gj_update_kernel(float* __restrict__ M, int r, int k0, int bk,
+                                                        const float* __restrict__ R, const float* __restrict__ C) {
+  __shared__ float Cs[64][GJB + 1];  // Cs[row][t]
+  __shared__ float Rs[GJB][64 + 1];  // Rs[t][col]
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64, tid = threadIdx.x;
+  for (int e = tid; e < 64 * GJB; e += 256) {
+    const int a = e / GJB, t = e % GJB;
+    Cs[a][t] = (i0 + a < r && t < bk) ? C[(long long)(i0 + a) * GJB + t] : 0.0f;
+    const int t2 = e / 64, b = e % 64;
+    Rs[t2][b] = (j0 + b < r && t2 < bk) ? R[(long long)t2 * r + j0 + b] : 0.0f;
+  }
+  __syncthreads();
+  const int ti = (tid / 16) * 4, tj = (tid % 16) * 4;
+  float acc[4][4] = {};
+  for (int t = 0; t < bk; t++) {
+    float c[4], q[4];
+#pragma unroll
+    for (int a = 0; a < 4; a++) c[a] = Cs[ti + a][t];
+#pragma unroll
+    for (int b = 0; b < 4; b++) q[b] = Rs[t][tj + b];
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+      for (int b = 0; b < 4; b++) acc[a][b] += c[a] * q[b];
+  }
+#pragma unroll
+  for (int a = 0; a < 4; a++) {
+    const int i = i0 + ti + a;
+    if (i >= r) continue;
+    const bool iK = i >= k0 && i < k0 + bk;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int j = j0 + tj + b;
+      if (j >= r) continue;
+      const bool jK = j >= k0 && j < k0 + bk;
+      float* mp = M + (long long)i * r + j;
+      *mp = iK ? R[(long long)(i - k0) * r + j] : (jK ? 0.0f : *mp) - acc[a][b];
+    }
+  }
 }
 
 // y = x + z elementwise (the projection input A + L).
@@ -289,6 +376,7 @@ inline unsigned blocks(long long n, int t) { return (unsigned)((n + t - 1) / t);
 struct AdmmWs {
   float *A, *B, *ZA, *ZB, *LA, *LB, *T, *G, *Gi;
   float *pA, *qA, *pB, *qB, *pv, *qv, *part, *sig, *sc;
+  float *Pinv, *R, *C;
 };
 
 AdmmWs ws_layout(uint8_t* base, int m, int n, int r, size_t* total) {
@@ -319,6 +407,9 @@ AdmmWs ws_layout(uint8_t* base, int m, int n, int r, size_t* total) {
   w.part = take((size_t)COL_CHUNKS * r);
   w.sig = take(4);
   w.sc = take(4);
+  w.Pinv = take((size_t)GJB * GJB);
+  w.R = take((size_t)GJB * r);
+  w.C = take((size_t)GJB * r);
   *total = o;
   return w;
 }
@@ -333,18 +424,15 @@ void gemm(hipStream_t st, int epi, const float* A, long long sai, long long sak,
   else hipLaunchKernelGGL(gemm_f32_kernel<0>, grid, dim3(256), 0, st, g);
 }
 
-// G (r x r, SPD) -> its inverse in `dst` (G is overwritten: the sweeps
-// alternate between the two buffers and the last one lands in dst).
-void spd_inverse(hipStream_t st, float* G, float* Gi, int r, float** dst) {
-  float* in = G;
-  float* out = Gi;
-  for (int k = 0; k < r; k++) {
-    hipLaunchKernelGGL(gj_sweep_kernel, dim3(blocks((long long)r * r, 256)), dim3(256), 0, st, in, out, r, k);
-    float* t = in;
-    in = out;
-    out = t;
+// G (r x r, SPD) -> its inverse, in place (block Gauss-Jordan, GJB pivots a step).
+void spd_inverse(hipStream_t st, const AdmmWs& w, float* G, int r) {
+  for (int k0 = 0; k0 < r; k0 += GJB) {
+    const int bk = r - k0 < GJB ? r - k0 : GJB;
+    hipLaunchKernelGGL(gj_block_inv_kernel, dim3(1), dim3(1024), 0, st, G, r, k0, bk, w.Pinv);
+    hipLaunchKernelGGL(gj_panel_kernel, dim3(blocks(r, 256), bk), dim3(256), 0, st, G, r, k0, bk, w.Pinv, w.R, w.C);
+    hipLaunchKernelGGL(gj_update_kernel, dim3(blocks(r, 64), blocks(r, 64)), dim3(256), 0, st, G, r, k0, bk, w.R,
+                       w.C);
   }
-  *dst = in;
 }
 
 // proj(Y) of a rows x r matrix: Z, optional dual update with X, optional
@@ -402,15 +490,15 @@ hipError_t admm_run(const AdmmArgs& a) {
   if (a.err) rel_err(st, w, a.W, m, n, r, a.err);
   for (int t = 0; t < a.iters; t++) {
     const bool last = t == a.iters - 1;
-    float* Ginv = nullptr;
+    const float* Ginv = w.G;
     // A <- (W B + rho (ZA - LA)) (B^T B + rho I)^-1
     gemm(st, 2, w.B, 1, r, w.B, r, 1, w.G, r, r, r, n, nullptr, nullptr, 0, a.rho);
-    spd_inverse(st, w.G, w.Gi, r, &Ginv);
+    spd_inverse(st, w, w.G, r);
     gemm(st, 1, a.W, n, 1, w.B, r, 1, w.T, r, m, r, n, w.ZA, w.LA, r, a.rho);
     gemm(st, 0, w.T, r, 1, Ginv, r, 1, w.A, r, m, r, r);
     // B <- (W^T A + rho (ZB - LB)) (A^T A + rho I)^-1
     gemm(st, 2, w.A, 1, r, w.A, r, 1, w.G, r, r, r, m, nullptr, nullptr, 0, a.rho);
-    spd_inverse(st, w.G, w.Gi, r, &Ginv);
+    spd_inverse(st, w, w.G, r);
     gemm(st, 1, a.W, 1, n, w.A, r, 1, w.T, r, n, r, m, w.ZB, w.LB, r, a.rho);
     gemm(st, 0, w.T, r, 1, Ginv, r, 1, w.B, r, n, r, r);
     // ZA <- proj(A + LA), LA += A - ZA; the same for B
