@@ -43,6 +43,8 @@ constexpr int TARGET_WG = 256;          // one workgroup per CU of an MI355X
 constexpr int MIN_WG = 128;             // fewest workgroups a stage is cut into (half the CUs)
 constexpr int WAVE_BUDGET = 256 * 12;   // resident waves of the chip at <= 168 VGPRs (3 per SIMD)
 constexpr int MIN_ROW_WAVES = 256;      // fewest waves a row-split stage 2 may have
+constexpr int TALL_ROW_TILES = 2048;    // row tiles from which stage 2 takes two row tiles per wave
+constexpr int RM2_QUADS = 10;           // quads per row tile the two-row-tile waves hold (20-quad buffer)
 constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles
 constexpr size_t LDS_S1 = 64 * 1024;    // image bytes a stage-1 workgroup may stage
 constexpr size_t LDS_S2 = 64 * 1024;    // image (+ reduction) bytes of a stage-2 workgroup
@@ -431,20 +433,22 @@ __device__ inline int full_quads(int KT, int q0, int q1) {
 // are issued up front into a 16-quad (64-VGPR) buffer; then for every column
 // tile the B operand is read from LDS once and feeds one MFMA per row tile,
 // each row tile with its own accumulator.
-template <int RM>
+template <int RM, int QWT = 16 / RM>
 struct WaveWork {
-  static constexpr int QW = 16 / RM;
+  static constexpr int QW = QWT;
   u4v w[RM][QW];
   int rt0, qa, qb, nfull;
 };
 
-// Issues the wave's RM x QW = 16 quad loads, always 16 and without a branch:
+// Issues the wave's RM x QW quad loads (16, or 20 for the two-row-tile waves
+// of tall stages), always all of them and without a branch:
 // a wave with no full quad re-reads the matrix's first 1 KiB (inside the blob
 // for every shape) and ignores it.  With a fixed count the compiler waits for
 // the prologue's loads (issued earlier) without waiting for these.
-template <int RM>
-__device__ __forceinline__ void wave_load(const uint32_t* __restrict__ P, int KT, int RT, WaveWork<RM>& ww, int lane) {
-  constexpr int QW = WaveWork<RM>::QW;
+template <int RM, int QWT>
+__device__ __forceinline__ void wave_load(const uint32_t* __restrict__ P, int KT, int RT, WaveWork<RM, QWT>& ww,
+                                          int lane) {
+  constexpr int QW = QWT;
   ww.nfull = full_quads(KT, ww.qa, ww.qb);
   const bool any = ww.nfull > 0;
   const int last = ww.qa + ww.nfull - 1;
@@ -468,10 +472,10 @@ __device__ __forceinline__ v8i image_b(const LaneImg<CW>& im, int kl, int* sb) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int CW, int RM>
-__device__ __forceinline__ void wave_mma(const uint32_t* __restrict__ P, int KT, int RT, const WaveWork<RM>& ww,
+template <int CW, int RM, int QWT>
+__device__ __forceinline__ void wave_mma(const uint32_t* __restrict__ P, int KT, int RT, const WaveWork<RM, QWT>& ww,
                                          const LaneImg<CW>& im, int ktbase, int lane, v4f (&acc)[RM]) {
-  constexpr int QW = WaveWork<RM>::QW;
+  constexpr int QW = QWT;
 #pragma unroll
   for (int j = 0; j < QW; j++) {
     if (j < ww.nfull) {
@@ -758,13 +762,13 @@ __device__ __forceinline__ void s2_body(const S2Args& a, int rowgroup, uint8_t* 
 // cross waves and the workgroup of W waves shares one encoded t' among W x RM
 // row tiles (fewer workgroups, so fewer copies of t' to read and encode).
 // Row group `rowgroup` = row tiles [rowgroup * W * RM, + W * RM).
-template <typename ST, int BB, int RM, int SM>
+template <typename ST, int BB, int RM, int SM, int QW = 16 / RM>
 __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint8_t* lds) {
   constexpr int CW = 4 * BB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
-  WaveWork<RM> ww;
+  WaveWork<RM, QW> ww;
   ww.rt0 = (rowgroup * W + wave) * RM;
   const int RG = min(RM, a.RT - ww.rt0);  // rows of this wave (<= 0: none; its loads are clamped)
   ww.qa = 0;
@@ -775,7 +779,7 @@ __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint
   const int per_pass = TPass<ST, SM, BB>::CPT * blockDim.x, total = BB * a.KT * 16;
   TPass<ST, SM, BB> tp;
   tp.load(a.part, a.S1, a.Rpad1, g, a.r, a.KT, 0);  // prologue loads first, then the weight stream
-  wave_load<RM>(a.u, a.KT, a.RT, ww, lane);
+  wave_load<RM, QW>(a.u, a.KT, a.RT, ww, lane);
   // output scales of this lane's four rows in each row tile (one word per tile,
   // clamped into the layer; used only for rows < m)
   Raw8<ST> s1w[RM];
@@ -807,7 +811,7 @@ __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint
   v4f acc[RM];
 #pragma unroll
   for (int r = 0; r < RM; r++) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
-  wave_mma<CW, RM>(a.u, a.KT, a.RT, ww, im, 0, lane, acc);
+  wave_mma<CW, RM, QW>(a.u, a.KT, a.RT, ww, im, 0, lane, acc);
   // columns 4b hold batch row b; with an envelope the env rows of one output
   // row are summed across lanes 4 and 8 apart (columns past the batch add 0)
   const bool valid = (c & 3) == 0 && b < BB && sr == 0;
@@ -846,10 +850,10 @@ __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint
 
 // BIG: more than 8 waves per workgroup (launch bound 1024 threads, so at most
 // 128 VGPRs: only the shapes the plan allows it for fit without spilling).
-template <typename ST, int BB, int RM, int SM, bool BIG>
+template <typename ST, int BB, int RM, int SM, bool BIG, int QW = 16 / RM>
 __global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_kernel(S2Args a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  s2_rows_body<ST, BB, RM, SM>(a, blockIdx.x, lds);
+  s2_rows_body<ST, BB, RM, SM, QW>(a, blockIdx.x, lds);
 }
 
 template <typename ST, bool FUSED, int BB, int RM, int SM>
@@ -875,7 +879,7 @@ __global__ void __launch_bounds__(512) dec_s2_group_kernel(S2Group g) {
   s2_body<ST, true, BB, RM, SM>(g.l[l], bx - begin, lds);
 }
 
-template <typename ST, int BB, int RM, int SM, bool BIG>
+template <typename ST, int BB, int RM, int SM, bool BIG, int QW = 16 / RM>
 __global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_group_kernel(S2Group g) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int bx = blockIdx.x;
@@ -883,7 +887,7 @@ __global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_group_kernel(S2G
 #pragma unroll
   for (int i = 0; i < MAX_GROUP - 1; i++) l += bx >= g.wg_end[i] ? 1 : 0;
   const int begin = l == 0 ? 0 : g.wg_end[l - 1];
-  s2_rows_body<ST, BB, RM, SM>(g.l[l], bx - begin, lds);
+  s2_rows_body<ST, BB, RM, SM, QW>(g.l[l], bx - begin, lds);
 }
 
 }  // namespace
@@ -921,6 +925,18 @@ static bool pick_shape(int RT, int splits, int quads, int minwg, int* RM, int* K
 static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_bytes, int min_waves, int* RM,
                       int* W) {
   if (quads > 16 || RT < min_waves) return false;  // few rows: the K-split keeps more waves busy
+  // Tall stages (the 70B gate+up pair: 3584 row tiles) run 16 waves per CU
+  // with one row tile per wave, and every wave reads the whole t' image from
+  // LDS as its B operand: 2 KiB per MFMA per wave, 1.28 MB per CU, which
+  // bounds the product phase by LDS bandwidth (measured 4.2 us of the
+  // stage's 14 us).  Two row tiles per wave (a 20-quad buffer, 8 waves per
+  // workgroup) read each B operand once for two MFMAs.
+  if (B == 1 && scale_bytes == 2 && S1 <= 2 && RT >= TALL_ROW_TILES && quads <= RM2_QUADS &&
+      chunks <= 2 * 64 * 8) {
+    *RM = 2;
+    *W = 8;
+    return true;
+  }
   // one row tile per wave: twice the waves and workgroups of two row tiles
   // per wave finish the products and the per-workgroup prologue sooner
   // (measured on the 70B chain: 2.6% less time per token)
@@ -1048,13 +1064,17 @@ static void launch_rows_t(int RM, bool big, dim3 g, dim3 b, size_t lds, hipStrea
     else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k);                   \
   } while (0)
   if constexpr (BB == 1 && SM <= 2 && sizeof(ST) == 2) {
+    if (RM == 2) {  // tall stages: two row tiles per wave, 8 waves (see pick_rows)
+      if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, 2, SM, false, RM2_QUADS>), g, b, lds, st, k);
+      else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, 2, SM, false, RM2_QUADS>), g, b, lds, st, k);
+      return;
+    }
     if (big) {  // the shapes with more than 8 waves (see pick_rows)
       NQ_ROWS(1, true);
       return;
     }
   }
-  NQ_ROWS(1, false);  // pick_rows gives every wave one row tile
-  (void)RM;
+  NQ_ROWS(1, false);  // otherwise pick_rows gives every wave one row tile
 #undef NQ_ROWS
 }
 
