@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="time the 560 linears one by one (no layer groups)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill section")
     ap.add_argument("--no-initializer", action="store_true", help="skip the ADMM initialiser section")
+    ap.add_argument("--no-variants", action="store_true", help="skip the transposed / envelope section")
+    ap.add_argument("--variants-only", action="store_true", help="run only the transposed / envelope section")
     ap.add_argument("--initializer-only", action="store_true", help="run only the ADMM initialiser section")
     ap.add_argument("--suite", default=None, choices=["7b"])
     ap.add_argument("--out", default=None)
@@ -587,6 +589,8 @@ def run_decode70b(args):
         out["prefill"] = run_prefill70b(dev)
     if not args.no_initializer:
         out["initializer"] = run_initializer(dev)
+    if not args.no_variants:
+        out["variants"] = run_variants(dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline ...")
         out["cpu_baseline"] = cpu_baseline(spec, B)
@@ -639,6 +643,54 @@ def run_initializer(dev, m=4096, n=4096, bpw=0.8, power_iters=8, rho=10.0):
             "ms_per_step": round(per, 3), "ms_setup_and_projection": round(t0, 3),
             "flops_per_step": gemm_flops + inv_flops, "tflops": round(tf, 2),
             "mfma_util_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "peak_tflops": FP32_MFMA_PEAK_TFLOPS}
+
+
+# ------------------------------------------------------------------ transposed product and envelope
+def run_variants(dev, copies=6, calls=48, bpw=0.8):
+    """One 70B gate-projection shape (28672 x 8192 at 0.8 bpw), B = 1, single
+    linears captured as a HIP graph of `calls` calls rotating over `copies`
+    layers (141 MB, beyond the caches): the forward y = x W_hat^T, the
+    transposed product dx = dy W_hat on the bit-transposed layer, and the rank-l
+    envelope forward for l = 2 and 4.  GB/s = algorithmic bytes per call
+    (sign bits, scales incl. the l envelope pairs, x, y) / time per call."""
+    import torch
+    import binary_rank_gemv_packed_amd as nq
+    m, n = 28672, 8192
+    r = nq.rank_for_bits(m, n, bpw, 16)
+    layers = [make_layer_gpu(m, n, r, 1, 900 + c, dev)[0] for c in range(copies)]
+    tlayers = [nq.transpose(L) for L in layers]
+    g = torch.Generator(device=dev)
+    g.manual_seed(20260206)
+    x = torch.randn(1, n, generator=g, device=dev).to(torch.bfloat16)
+    dy = torch.randn(1, m, generator=g, device=dev).to(torch.bfloat16)
+    s1e = (torch.randn(4, m, generator=g, device=dev).abs() + 0.1).half()
+    s2e = (torch.randn(4, n, generator=g, device=dev).abs() + 0.1).half()
+    stream = torch.cuda.Stream()
+    out = {"workload": f"llama2-70b gate shape {m}x{n}, r={r} (0.8 bpw), B=1, bf16, {copies} rotating copies"}
+
+    def measure(name, fn, bytes_per_call):
+        def step():
+            for k in range(calls):
+                fn(k % copies)
+        ms, _ = time_graph(torch, stream, step, 3, 10)
+        us = ms * 1e3 / calls
+        out[name] = {"us_per_call": round(us, 3), "gbs": round(bytes_per_call / us / 1e3, 1)}
+        log(f"[bench] {name}: {us:.2f} us per call, {out[name]['gbs']} GB/s")
+
+    base = r * (m + n) / 8 + 2 * r
+    measure("forward", lambda c: nq.linear(x, layers[c]), base + 2 * (m + n) + 2 * n + 2 * m)
+    measure("transposed", lambda c: nq.linear(dy, tlayers[c]), base + 2 * (m + n) + 2 * m + 2 * n)
+    for env in (2, 3, 4):
+        try:
+            measure(f"envelope_l{env}", lambda c, e=env: nq.linear_envelope(x, layers[c], s1e[:e], s2e[:e]),
+                    base + 2 * env * (m + n) + 2 * n + 2 * m)
+        except nq.NQError as e:  # the envelope's t' image for env terms must fit the workgroup's LDS
+            torch.cuda.synchronize()
+            out[f"envelope_l{env}"] = {"unsupported": str(e)}
+            log(f"[bench] envelope_l{env}: {e}")
+    del layers, tlayers
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------ 7B per-shape suite
@@ -883,6 +935,8 @@ def main():
         run_suite7b(args)
     elif args.initializer_only:
         print(json.dumps({"initializer": run_initializer("cuda:0")}), flush=True)
+    elif args.variants_only:
+        print(json.dumps({"variants": run_variants("cuda:0")}), flush=True)
     else:
         run_decode70b(args)
 
