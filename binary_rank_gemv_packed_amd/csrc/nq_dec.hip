@@ -48,6 +48,13 @@ constexpr int RM2_QUADS = 10;           // quads per row tile the two-row-tile w
 constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles
 constexpr size_t LDS_S1 = 64 * 1024;    // image bytes a stage-1 workgroup may stage
 constexpr size_t LDS_S2 = 64 * 1024;    // image (+ reduction) bytes of a stage-2 workgroup
+// LDS of one gfx950 workgroup (160 KiB).  A plan first keeps to the budgets
+// above (the measured shapes of the B = 1 and 2 chains); when that gives no
+// plan (three or four batch rows, or envelope terms, at ranks of several
+// thousand: the image of t' then needs 85 KiB at rank 5079) it is made again
+// with this budget for both stages, rather than falling back to chunks that
+// read the weights once per two batch rows.
+constexpr size_t LDS_MAX = 160 * 1024;
 
 // Image of a vector range of KL column tiles, for B batch rows (CW = 4B MFMA
 // columns in use):
@@ -951,7 +958,7 @@ static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_by
   return true;
 }
 
-DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows) {
+static DecPlan dec_plan_cap(int m, int n, int r, int B, int scale_bytes, bool force_rows, size_t cap1, size_t cap2) {
   DecPlan p{};
   p.ok = false;
   if (B < 1 || B > DEC_MAX_B) return p;
@@ -964,7 +971,7 @@ DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows) {
   p.RT1 = ceil_div(r, 16);
   p.KT1 = ceil_div(n, 128);
   const int quads1 = ceil_div(p.KT1, 4);
-  int klmax = (int)((LDS_S1 - red_bytes) / tb) / 4 * 4;
+  int klmax = (int)((cap1 - red_bytes) / tb) / 4 * 4;
   if (klmax < 4) return p;
   {
     int rm, ks;
@@ -1018,12 +1025,12 @@ DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows) {
   p.QM2 = ceil_div(quads2, p.KS2);
   p.red2 = align_up((size_t)p.KT2 * tb, 16);
   p.lds2 = p.red2 + red_bytes + S1_LDS_BYTES;
-  if (p.lds2 > LDS_S2) return p;
+  if (p.lds2 > cap2) return p;
   p.fused_mid = p.S1 * B <= 4 && p.S1 != 3;
   p.rows2 = false;
   {
     int rm, w;
-    if (p.fused_mid && pick_rows(p.RT2, quads2, B * p.KT2 * 16, p.S1, B, scale_bytes, force_rows ? 1 : MIN_ROW_WAVES, &rm, &w) && p.KT2 * tb <= LDS_S2) {
+    if (p.fused_mid && pick_rows(p.RT2, quads2, B * p.KT2 * 16, p.S1, B, scale_bytes, force_rows ? 1 : MIN_ROW_WAVES, &rm, &w) && p.KT2 * tb <= cap2) {
       p.rows2 = true;
       p.RG2 = rm;
       p.KS2 = w;
@@ -1043,6 +1050,11 @@ DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows) {
   p.bytes = o;
   p.ok = true;
   return p;
+}
+
+DecPlan dec_plan(int m, int n, int r, int B, int scale_bytes, bool force_rows) {
+  const DecPlan p = dec_plan_cap(m, n, r, B, scale_bytes, force_rows, LDS_S1, LDS_S2);
+  return p.ok ? p : dec_plan_cap(m, n, r, B, scale_bytes, force_rows, LDS_MAX, LDS_MAX);
 }
 
 template <typename ST, bool FUSED, int BB, int SM>
@@ -1178,7 +1190,8 @@ static hipError_t dec_forward_b(const FwdArgs& a, const DecPlan& p) {
   }
 }
 
-GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_bytes) {
+static GroupPlan group_plan_cap(const int* m, const int* r, int L, int n, int B, int scale_bytes, size_t cap1,
+                                size_t cap2) {
   GroupPlan p{};
   p.ok = false;
   if (L < 1 || L > GROUP_MAX || B < 1 || B > DEC_MAX_B) return p;
@@ -1201,7 +1214,7 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_
   }
   // stage 1: the rules of the single-layer plan, on the layers' rows together
   const int quads1 = ceil_div(p.KT1, 4);
-  const int klmax = (int)((LDS_S1 - red_bytes) / tb) / 4 * 4;
+  const int klmax = (int)((cap1 - red_bytes) / tb) / 4 * 4;
   if (klmax < 4) return p;
   {
     int rm, ks;
@@ -1211,6 +1224,7 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_
     int s = ceil_div(TARGET_WG, rowgroups);
     s = s > smax ? smax : s;
     s = s > quads1 ? quads1 : s;
+    s = s > 4 / B ? 4 / B : s;  // stage 2 folds the S1 x B partial vectors (<= 4) into its prologue
     s = s < 1 ? 1 : s;
     const int s_lds = ceil_div(p.KT1, klmax);
     if (s < s_lds) s = s_lds;
@@ -1243,7 +1257,7 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_
   }
   p.red2 = align_up((size_t)kt2max * tb, 16);
   p.lds2 = p.red2 + red_bytes + S1_LDS_BYTES;
-  if (p.lds2 > LDS_S2) return p;
+  if (p.lds2 > cap2) return p;
   p.rows2 = false;
   {
     int rm, w;
@@ -1278,6 +1292,11 @@ GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_
   p.bytes = o;
   p.ok = true;
   return p;
+}
+
+GroupPlan group_plan(const int* m, const int* r, int L, int n, int B, int scale_bytes) {
+  const GroupPlan p = group_plan_cap(m, r, L, n, B, scale_bytes, LDS_S1, LDS_S2);
+  return p.ok ? p : group_plan_cap(m, r, L, n, B, scale_bytes, LDS_MAX, LDS_MAX);
 }
 
 template <typename XT, typename ST, int BB>

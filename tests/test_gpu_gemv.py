@@ -190,3 +190,23 @@ def test_config4_llama70b_layer(name):
     L = synth.make_layer(m, n, r, 1, cfg=4, block=0, layer=synth.LAYER_ORDER.index(name))
     ref = G.oracle(L, "factored")
     assert G.rel_l2(G.run(L), ref) <= G.TOL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def test_config4_llama70b_batched(name):
+    """70B shapes at 0.8 bpw with B = 3, 4 and 16 on the decode path (one pass
+    over the weights per four batch rows: at these ranks the t' image of three
+    or four rows needs more than 64 KiB of LDS), every output against the
+    factored fp64 oracle, fp32 and bf16 outputs."""
+    m, n = synth.LLAMA70B[name]
+    r = O.rank_for_bits(m, n, 0.8, 16)
+    L16 = synth.make_layer(m, n, r, 16, cfg=4, block=1, layer=synth.LAYER_ORDER.index(name))
+    layer = G.pack_layer(L16)
+    for B in (3, 4, 16):
+        x = L16.x[:B]
+        ref = G.oracle(L16, "factored", x=x)
+        print(f"70b batched {name} B={B}", flush=True)
+        y32 = G.run(L16, layer, x_override=x, y_dtype=torch.float32, path="decode")
+        assert G.rel_l2(y32, ref) <= 3e-4, (B, G.rel_l2(y32, ref))
+        y = G.run(L16, layer, x_override=x, path="decode")
+        assert G.rel_l2(y, ref) <= G.TOL, (B, G.rel_l2(y, ref))

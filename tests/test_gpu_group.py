@@ -80,15 +80,17 @@ def test_group_deterministic():
 
 
 @pytest.mark.parametrize("which", ["qkv", "gate_up"])
-def test_config4_llama70b_groups(which):
-    """The 70B block's shared-input groups at 0.8 bpw, B = 1, each output
-    against the factored fp64 oracle of its layer."""
+@pytest.mark.parametrize("B", [1, 4])
+def test_config4_llama70b_groups(which, B):
+    """The 70B block's shared-input groups at 0.8 bpw, B = 1 and 4 (at B = 4
+    the plan needs more than 64 KiB of LDS per workgroup), each output against
+    the factored fp64 oracle of its layer."""
     names = ["q", "k", "v"] if which == "qkv" else ["gate", "up"]
     Ls = []
     for i, nm in enumerate(names):
         m, n = synth.LLAMA70B[nm]
         r = nq.rank_for_bits(m, n, 0.8, 16)
-        Ls.append(synth.make_layer(m, n, r, 1, cfg=4, block=0, layer=synth.LAYER_ORDER.index(nm)))
+        Ls.append(synth.make_layer(m, n, r, B, cfg=4, block=0, layer=synth.LAYER_ORDER.index(nm)))
     for L in Ls[1:]:
         L.x = Ls[0].x
     layers = [G.pack_layer(L) for L in Ls]
