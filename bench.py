@@ -468,7 +468,7 @@ def run_decode70b(args):
     dev = "cuda:0"
     B = args.batch
     spec = chain_spec(synth.LLAMA70B, 80, args.bpw)
-    fused = not args.unfused and B <= 4 and args.path == "auto"
+    fused = not args.unfused and args.path == "auto"
     check_ids = {0: "q", 1: "k", 4: "gate", 6: "down"}  # one linear per distinct shape of block 0
     layers, xs, ys, hosts = [], [], [], {}
     t0 = time.time()

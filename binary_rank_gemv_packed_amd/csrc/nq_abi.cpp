@@ -453,10 +453,28 @@ static nq_status check_group(const nq_layer* const* layers, int32_t L) {
   return NQ_OK;
 }
 
+// Batch rows per pass of the fused group path for a batch of B rows: the
+// largest of min(B, 4) .. 1 that has a group plan (0: none).  Larger batches
+// run as consecutive passes of that many rows, each reading the weights again.
+static int group_chunk(const nq_layer* const* layers, int32_t L, int32_t B) {
+  for (int c = B < 4 ? B : 4; c >= 1; c--)
+    if (group_plan_of(layers, L, c).ok) return c;
+  return 0;
+}
+
 size_t nq_workspace_bytes_group(const nq_layer* const* layers, int32_t L, int32_t B) {
   if (check_group(layers, L) || B <= 0 || B > MAX_BATCH) return 0;
   const nq::GroupPlan p = group_plan_of(layers, L, B);
   if (p.ok) return p.bytes;
+  const int c = group_chunk(layers, L, B);
+  if (c) {  // passes of c rows (and one of B mod c)
+    size_t need = group_plan_of(layers, L, c).bytes;
+    if (B % c) {
+      const nq::GroupPlan t = group_plan_of(layers, L, B % c);
+      if (t.ok && t.bytes > need) need = t.bytes;
+    }
+    return need;
+  }
   size_t need = 0;  // one layer after another
   for (int l = 0; l < L; l++) {
     const size_t b = plan_bytes(layers[l], B, auto_path(layers[l], B));
@@ -494,6 +512,36 @@ static nq_status group_impl(const nq_layer* const* layers, int32_t L, const void
     return fail(NQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
   if (need && !workspace) return fail(NQ_ERR_INVALID_ARG, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(NQ_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const int chunk = p.ok ? B : group_chunk(layers, L, B);
+  if (!p.ok && chunk) {  // passes of `chunk` batch rows through the fused group path
+    if (marks) return fail(NQ_ERR_UNSUPPORTED, "timing marks need a single pass of the fused group path (B <= 4)");
+    for (int b0 = 0; b0 < B; b0 += chunk) {
+      const int cb = B - b0 < chunk ? B - b0 : chunk;
+      const nq::GroupPlan pc = group_plan_of(layers, L, cb);
+      if (!pc.ok) return fail(NQ_ERR_INTERNAL, "no group plan for a pass of %d rows", cb);
+      nq::GroupArgs a;
+      a.L = L;
+      a.n = layers[0]->n;
+      a.B = cb;
+      for (int l = 0; l < L; l++) {
+        a.m[l] = layers[l]->m;
+        a.r[l] = layers[l]->r;
+        a.blob[l] = static_cast<const uint8_t*>(layers[l]->blob);
+        a.y[l] = static_cast<uint8_t*>(ys[l]) + (size_t)b0 * layers[l]->m * yb;
+      }
+      a.scale_dtype = layers[0]->scale_dtype;
+      a.x_dtype = x_dtype;
+      a.y_dtype = y_dtype;
+      a.x = static_cast<const uint8_t*>(x) + (size_t)b0 * layers[0]->n * xb;
+      a.ws = static_cast<uint8_t*>(workspace);
+      a.stream = reinterpret_cast<hipStream_t>(stream);
+      a.marks = nullptr;
+      (void)hipGetLastError();
+      const hipError_t e = nq::group_forward(a, pc);
+      if (e != hipSuccess) return hip_fail(e, "group forward launch");
+    }
+    return ok();
+  }
   if (!p.ok) {
     if (marks) return fail(NQ_ERR_UNSUPPORTED, "timing marks need the fused group path (B <= 4)");
     for (int l = 0; l < L; l++) {  // one layer after another, each on its automatic path

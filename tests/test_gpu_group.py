@@ -1,7 +1,7 @@
 """GPU: layer groups (q/k/v and gate/up share x) through nq_linear_fwd_group:
 every output against the fp64 oracle of its own layer, bit equality with the
-single-layer decode path where the plans coincide, and the large-batch
-fallback equal to the single-layer calls."""
+single-layer decode path where the plans coincide, and large batches as
+passes of four rows."""
 import numpy as np
 import pytest
 import torch
@@ -65,11 +65,21 @@ def test_single_layer_group_equals_decode_path_bit_for_bit():
 
 
 @pytest.mark.parametrize("B", [5, 17])
-def test_group_beyond_fused_batch_runs_layer_by_layer(B):
+def test_group_beyond_fused_batch_runs_in_passes(B):
+    """B > 4 runs as passes of four rows (and one of B mod 4) through the fused
+    group path: every output against the oracle, and every pass equal bit for
+    bit to the group call on its rows alone."""
     Ls, layers = _group([(300, 129), (64, 40)], 520, B, cfg=39)
     yg = _run_group(Ls, layers, torch.float32)
-    for L, layer, y in zip(Ls, layers, yg):
-        assert np.array_equal(y, G.run(L, layer, y_dtype=torch.float32, path="auto"))
+    for L, y in zip(Ls, yg):
+        assert G.rel_l2(y, G.oracle(L, "factored")) <= 3e-4
+    x_all = Ls[0].x
+    for b0 in range(0, B, 4):
+        for L in Ls:
+            L.x = x_all[b0:b0 + 4]
+        part = _run_group(Ls, layers, torch.float32)
+        for y, yp in zip(yg, part):
+            assert np.array_equal(y[b0:b0 + 4], yp)
 
 
 def test_group_deterministic():
