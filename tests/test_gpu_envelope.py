@@ -93,3 +93,19 @@ def test_envelope_beyond_four_rows_is_unsupported():
     with pytest.raises(nq.NQError) as e:
         _run(L, G.pack_layer(L), S1, S2, torch.float32)
     assert e.value.status == nq.NQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("env,B", [(3, 1), (4, 1), (2, 2)])
+def test_envelope_parity_70b_rank(env, B):
+    """Rank 5079 (the 70B gate/up/down rank at 0.8 bpw): three and four terms
+    need the plans that use more than 64 KiB of LDS per workgroup."""
+    m, n, r = 2048, 8192, 5079
+    L, S1, S2 = _env_case(m, n, r, B, env, cfg=61)
+    layer = G.pack_layer(L)
+    ref = O.linear_envelope_factored(L.x.astype(np.float64), L.U, L.V, S1.astype(np.float64),
+                                     L.g.astype(np.float64), S2.astype(np.float64))
+    print(f"envelope 70b rank env={env} B={B}", flush=True)
+    y32 = _run(L, layer, S1, S2, torch.float32)
+    ybf = _run(L, layer, S1, S2, torch.bfloat16)
+    assert G.rel_l2(y32, ref) <= 3e-4
+    G.check_bf16_output(ybf, ref, y32)
