@@ -271,9 +271,9 @@ struct XPass {
 // tiles into an LDS image, CPT chunks (all splits) per thread per pass; split
 // into loads and encoding like XPass, and branch-free like it (split indices
 // past S1 re-read split S1 - 1 and are left out of the sum).
-template <typename ST, int SM, int BB>
+template <typename ST, int SM, int BB, int CPTV = 2>
 struct TPass {
-  static constexpr int CPT = 2;
+  static constexpr int CPT = CPTV;
   float4 pv[CPT][SM][2];
   Raw8<ST> rg[CPT];
 
@@ -769,7 +769,7 @@ __device__ __forceinline__ void s2_body(const S2Args& a, int rowgroup, uint8_t* 
 // cross waves and the workgroup of W waves shares one encoded t' among W x RM
 // row tiles (fewer workgroups, so fewer copies of t' to read and encode).
 // Row group `rowgroup` = row tiles [rowgroup * W * RM, + W * RM).
-template <typename ST, int BB, int RM, int SM, int QW = 16 / RM>
+template <typename ST, int BB, int RM, int SM, int QW = 16 / RM, int CPT = 2>
 __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint8_t* lds) {
   constexpr int CW = 4 * BB;
   const int lane = threadIdx.x & 63;
@@ -783,8 +783,8 @@ __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint
   const Img li = img_at(lds, a.KT, CW);
   const ST* g = reinterpret_cast<const ST*>(a.g);
   const ST* s1 = reinterpret_cast<const ST*>(a.s1);
-  const int per_pass = TPass<ST, SM, BB>::CPT * blockDim.x, total = BB * a.KT * 16;
-  TPass<ST, SM, BB> tp;
+  const int per_pass = TPass<ST, SM, BB, CPT>::CPT * blockDim.x, total = BB * a.KT * 16;
+  TPass<ST, SM, BB, CPT> tp;
   tp.load(a.part, a.S1, a.Rpad1, g, a.r, a.KT, 0);  // prologue loads first, then the weight stream
   wave_load<RM, QW>(a.u, a.KT, a.RT, ww, lane);
   // output scales of this lane's four rows in each row tile (one word per tile,
@@ -857,10 +857,10 @@ __device__ __forceinline__ void s2_rows_body(const S2Args& a, int rowgroup, uint
 
 // BIG: more than 8 waves per workgroup (launch bound 1024 threads, so at most
 // 128 VGPRs: only the shapes the plan allows it for fit without spilling).
-template <typename ST, int BB, int RM, int SM, bool BIG, int QW = 16 / RM>
+template <typename ST, int BB, int RM, int SM, bool BIG, int QW = 16 / RM, int CPT = 2>
 __global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_kernel(S2Args a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  s2_rows_body<ST, BB, RM, SM, QW>(a, blockIdx.x, lds);
+  s2_rows_body<ST, BB, RM, SM, QW, CPT>(a, blockIdx.x, lds);
 }
 
 template <typename ST, bool FUSED, int BB, int RM, int SM>
@@ -886,7 +886,7 @@ __global__ void __launch_bounds__(512) dec_s2_group_kernel(S2Group g) {
   s2_body<ST, true, BB, RM, SM>(g.l[l], bx - begin, lds);
 }
 
-template <typename ST, int BB, int RM, int SM, bool BIG, int QW = 16 / RM>
+template <typename ST, int BB, int RM, int SM, bool BIG, int QW = 16 / RM, int CPT = 2>
 __global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_group_kernel(S2Group g) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int bx = blockIdx.x;
@@ -894,7 +894,7 @@ __global__ void __launch_bounds__(BIG ? 1024 : 512) dec_s2_rows_group_kernel(S2G
 #pragma unroll
   for (int i = 0; i < MAX_GROUP - 1; i++) l += bx >= g.wg_end[i] ? 1 : 0;
   const int begin = l == 0 ? 0 : g.wg_end[l - 1];
-  s2_rows_body<ST, BB, RM, SM, QW>(g.l[l], bx - begin, lds);
+  s2_rows_body<ST, BB, RM, SM, QW, CPT>(g.l[l], bx - begin, lds);
 }
 
 }  // namespace
@@ -938,8 +938,8 @@ static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_by
   // bounds the product phase by LDS bandwidth (measured 4.2 us of the
   // stage's 14 us).  Two row tiles per wave (a 20-quad buffer, 8 waves per
   // workgroup) read each B operand once for two MFMAs.
-  if (B == 1 && scale_bytes == 2 && S1 <= 2 && RT >= TALL_ROW_TILES && quads <= RM2_QUADS &&
-      chunks <= 2 * 64 * 8) {
+  if (B <= 2 && scale_bytes == 2 && S1 <= 2 && RT >= TALL_ROW_TILES && quads <= RM2_QUADS &&
+      chunks <= (B == 1 ? 2 : 3) * 64 * 8) {  // the prologue in one pass (2 or 3 chunks per thread)
     *RM = 2;
     *W = 8;
     return true;
@@ -1075,12 +1075,15 @@ static void launch_rows_t(int RM, bool big, dim3 g, dim3 b, size_t lds, hipStrea
     if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k); \
     else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k);                   \
   } while (0)
-  if constexpr (BB == 1 && SM <= 2 && sizeof(ST) == 2) {
+  if constexpr (BB <= 2 && SM <= 2 && sizeof(ST) == 2) {
     if (RM == 2) {  // tall stages: two row tiles per wave, 8 waves (see pick_rows)
-      if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, 2, SM, false, RM2_QUADS>), g, b, lds, st, k);
-      else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, 2, SM, false, RM2_QUADS>), g, b, lds, st, k);
+      constexpr int CPT = BB == 1 ? 2 : 3;  // the prologue in one pass of 512 threads
+      if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, 2, SM, false, RM2_QUADS, CPT>), g, b, lds, st, k);
+      else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, 2, SM, false, RM2_QUADS, CPT>), g, b, lds, st, k);
       return;
     }
+  }
+  if constexpr (BB == 1 && SM <= 2 && sizeof(ST) == 2) {
     if (big) {  // the shapes with more than 8 waves (see pick_rows)
       NQ_ROWS(1, true);
       return;
