@@ -45,6 +45,9 @@ constexpr int WAVE_BUDGET = 256 * 12;   // resident waves of the chip at <= 168 
 constexpr int MIN_ROW_WAVES = 256;      // fewest waves a row-split stage 2 may have
 constexpr int TALL_ROW_TILES = 2048;    // row tiles from which stage 2 takes two row tiles per wave
 constexpr int RM2_QUADS = 10;           // quads per row tile the two-row-tile waves hold (20-quad buffer)
+// prologue chunks per thread of the two-row-tile stage 2 for B batch rows:
+// enough for B x 10 quads x 64 chunks in one pass of 512 threads
+__host__ __device__ constexpr int rm2_chunks_per_thread(int B) { return B == 1 ? 2 : (B == 2 ? 3 : (B == 3 ? 4 : 5)); }
 constexpr size_t S1_LDS_BYTES = 8 * 16 * 4;  // output scales of a stage-2 workgroup's <= 8 row tiles
 constexpr size_t LDS_S1 = 64 * 1024;    // image bytes a stage-1 workgroup may stage
 constexpr size_t LDS_S2 = 64 * 1024;    // image (+ reduction) bytes of a stage-2 workgroup
@@ -938,8 +941,8 @@ static bool pick_rows(int RT, int quads, int chunks, int S1, int B, int scale_by
   // bounds the product phase by LDS bandwidth (measured 4.2 us of the
   // stage's 14 us).  Two row tiles per wave (a 20-quad buffer, 8 waves per
   // workgroup) read each B operand once for two MFMAs.
-  if (B <= 2 && scale_bytes == 2 && S1 <= 2 && RT >= TALL_ROW_TILES && quads <= RM2_QUADS &&
-      chunks <= (B == 1 ? 2 : 3) * 64 * 8) {  // the prologue in one pass (2 or 3 chunks per thread)
+  if (scale_bytes == 2 && S1 <= 2 && RT >= TALL_ROW_TILES && quads <= RM2_QUADS &&
+      chunks <= rm2_chunks_per_thread(B) * 64 * 8) {  // the prologue in one pass
     *RM = 2;
     *W = 8;
     return true;
@@ -1075,9 +1078,9 @@ static void launch_rows_t(int RM, bool big, dim3 g, dim3 b, size_t lds, hipStrea
     if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k); \
     else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, R, SM, BIGV>), g, b, lds, st, k);                   \
   } while (0)
-  if constexpr (BB <= 2 && SM <= 2 && sizeof(ST) == 2) {
+  if constexpr (SM <= 2 && sizeof(ST) == 2) {
     if (RM == 2) {  // tall stages: two row tiles per wave, 8 waves (see pick_rows)
-      constexpr int CPT = BB == 1 ? 2 : 3;  // the prologue in one pass of 512 threads
+      constexpr int CPT = rm2_chunks_per_thread(BB);  // the prologue in one pass of 512 threads
       if constexpr (GROUP) hipLaunchKernelGGL((dec_s2_rows_group_kernel<ST, BB, 2, SM, false, RM2_QUADS, CPT>), g, b, lds, st, k);
       else hipLaunchKernelGGL((dec_s2_rows_kernel<ST, BB, 2, SM, false, RM2_QUADS, CPT>), g, b, lds, st, k);
       return;
