@@ -666,7 +666,7 @@ nq_status nq_read_probe(const void* buf, size_t bytes, uint32_t* sink, nq_stream
 }
 
 size_t nq_admm_workspace_bytes(int32_t m, int32_t n, int32_t r) {
-  if (!dims_ok(m, n, r) || r > 4096 || r > m || r > n) return 0;
+  if (!dims_ok(m, n, r) || r > 4096 || r > m || r > n || (long long)(m > n ? m : n) * r >= (1LL << 31)) return 0;
   return nq::admm_workspace_bytes(m, n, r);
 }
 
@@ -678,6 +678,8 @@ nq_status nq_admm_factorize(const float* W, int32_t m, int32_t n, int32_t r, con
     return fail(NQ_ERR_INVALID_ARG, "W, A0, B0, U, V, s1, g, s2 and workspace must be given");
   if (!dims_ok(m, n, r) || r > 4096 || r > m || r > n)
     return fail(NQ_ERR_INVALID_ARG, "dimensions out of range: m=%d n=%d r=%d (r <= min(m, n, 4096))", m, n, r);
+  if ((long long)(m > n ? m : n) * r >= (1LL << 31))
+    return fail(NQ_ERR_INVALID_ARG, "max(m, n) x r = %lld elements (below 2^31 required)", (long long)(m > n ? m : n) * r);
   if (!(rho > 0.0f) || !std::isfinite(rho)) return fail(NQ_ERR_INVALID_ARG, "rho must be positive and finite");
   if (iters < 0 || iters > 10000 || power_iters < 0 || power_iters > 1000)
     return fail(NQ_ERR_INVALID_ARG, "iters (%d) must be in 0..10000, power_iters (%d) in 0..1000", iters, power_iters);

@@ -296,8 +296,8 @@ __global__ void __launch_bounds__(1024) normalize_kernel(const float* __restrict
   if (threadIdx.x == 0 && norm_out) *norm_out = nrm;
 }
 
-__global__ void __launch_bounds__(256) fill_kernel(float* __restrict__ v, int n, float val) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
+__global__ void __launch_bounds__(256) fill_kernel(float* __restrict__ v, long long n, float val) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   if (e < n) v[e] = val;
 }
 
@@ -439,8 +439,8 @@ void spd_inverse(hipStream_t st, const AdmmWs& w, float* G, int r) {
 // signs; the scaled singular vectors go to ps (rows) and qs (r).
 void project(hipStream_t st, const AdmmWs& w, const float* Y, int rows, int r, int K, float* Z, float* L,
              const float* X, int8_t* S, float* ps, float* qs) {
-  hipLaunchKernelGGL(fill_kernel, dim3(blocks(r, 256)), dim3(256), 0, st, w.qv, r, 1.0f / sqrtf((float)r));
-  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, w.sig, 1, 0.0f);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks(r, 256)), dim3(256), 0, st, w.qv, (long long)r, 1.0f / sqrtf((float)r));
+  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, w.sig, 1LL, 0.0f);
   for (int it = 0; it < K; it++) {
     hipLaunchKernelGGL(absmv_rows_kernel, dim3(blocks(rows, 4)), dim3(256), 0, st, Y, rows, r, w.qv, w.pv);
     hipLaunchKernelGGL(normalize_kernel, dim3(1), dim3(1024), 0, st, nullptr, w.pv, rows, nullptr);
@@ -448,7 +448,7 @@ void project(hipStream_t st, const AdmmWs& w, const float* Y, int rows, int r, i
                        w.part);
     hipLaunchKernelGGL(normalize_kernel, dim3(1), dim3(1024), 0, st, w.part, w.qv, r, w.sig);
   }
-  if (K == 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks(rows, 256)), dim3(256), 0, st, w.pv, rows, 0.0f);
+  if (K == 0) hipLaunchKernelGGL(fill_kernel, dim3(blocks(rows, 256)), dim3(256), 0, st, w.pv, (long long)rows, 0.0f);
   hipLaunchKernelGGL(finish_proj_kernel, dim3(blocks((long long)rows * r, 256)), dim3(256), 0, st, Y, rows, r, w.pv,
                      w.qv, w.sig, Z, L, X, S);
   hipLaunchKernelGGL(scale_vec_kernel, dim3(blocks(rows, 256)), dim3(256), 0, st, w.pv, w.sig, ps, rows, nullptr);
@@ -482,8 +482,8 @@ hipError_t admm_run(const AdmmArgs& a) {
   const long long mr = (long long)m * r, nr = (long long)n * r;
   hipMemcpyAsync(w.A, a.A0, mr * 4, hipMemcpyDeviceToDevice, st);
   hipMemcpyAsync(w.B, a.B0, nr * 4, hipMemcpyDeviceToDevice, st);
-  hipLaunchKernelGGL(fill_kernel, dim3(blocks(mr, 256)), dim3(256), 0, st, w.LA, (int)mr, 0.0f);
-  hipLaunchKernelGGL(fill_kernel, dim3(blocks(nr, 256)), dim3(256), 0, st, w.LB, (int)nr, 0.0f);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks(mr, 256)), dim3(256), 0, st, w.LA, mr, 0.0f);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks(nr, 256)), dim3(256), 0, st, w.LB, nr, 0.0f);
   const bool last0 = a.iters == 0;
   project(st, w, w.A, m, r, a.power_iters, w.ZA, nullptr, nullptr, last0 ? a.U : nullptr, w.pA, w.qA);
   project(st, w, w.B, n, r, a.power_iters, w.ZB, nullptr, nullptr, last0 ? a.V : nullptr, w.pB, w.qB);
@@ -511,7 +511,7 @@ hipError_t admm_run(const AdmmArgs& a) {
   // s1 = pA, g = qA * qB, s2 = pB (the scaled vectors of the last projections)
   hipMemcpyAsync(a.s1, w.pA, (size_t)m * 4, hipMemcpyDeviceToDevice, st);
   hipMemcpyAsync(a.s2, w.pB, (size_t)n * 4, hipMemcpyDeviceToDevice, st);
-  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, w.sc + 3, 1, 1.0f);
+  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(256), 0, st, w.sc + 3, 1LL, 1.0f);
   hipLaunchKernelGGL(scale_vec_kernel, dim3(blocks(r, 256)), dim3(256), 0, st, w.qA, w.sc + 3, a.g, r, w.qB);
   return hipGetLastError();
 }

@@ -234,9 +234,9 @@ nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dty
  * aligned, not overlapping the outputs or the workspace.  All arithmetic is
  * fp32 (MFMA products, Gauss-Jordan inverse of the r x r Gram matrices) with
  * fixed reduction orders: repeated calls give identical bits.  rho > 0,
- * 0 <= iters <= 10000, 0 <= power_iters <= 1000, r <= min(m, n, 4096);
- * NQ_ERR_INVALID_ARG otherwise, NQ_ERR_WORKSPACE for a short workspace.
- * Asynchronous on `stream`. */
+ * 0 <= iters <= 10000, 0 <= power_iters <= 1000, r <= min(m, n, 4096),
+ * max(m, n) x r < 2^31, else NQ_ERR_INVALID_ARG; NQ_ERR_WORKSPACE for a
+ * short workspace.  err is NaN when W is all zeros.  Asynchronous on `stream`. */
 size_t nq_admm_workspace_bytes(int32_t m, int32_t n, int32_t r);
 nq_status nq_admm_factorize(const float* W, int32_t m, int32_t n, int32_t r, const float* A0, const float* B0,
                             float rho, int32_t iters, int32_t power_iters, int8_t* U, int8_t* V, float* s1,
