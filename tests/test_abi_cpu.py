@@ -264,6 +264,7 @@ def test_admm_validation(L):
     assert ws_need > 0
     assert L.nq_admm_workspace_bytes(64, 48, 49) == 0  # r > min(m, n)
     assert L.nq_admm_workspace_bytes(0, 48, 8) == 0
+    assert L.nq_admm_workspace_bytes(1 << 20, 1 << 20, 4096) == 0  # max(m, n) x r >= 2^31
     P = FAKE
     args = dict(W=P, m=64, n=48, r=8, A0=P, B0=P, rho=1.0, iters=2, K=3, U=P, V=P, s1=P, g=P, s2=P, err=None,
                 ws=P, wsb=ws_need)
@@ -275,6 +276,7 @@ def test_admm_validation(L):
     assert call(W=None) == nq.NQ_ERR_INVALID_ARG
     assert call(s2=None) == nq.NQ_ERR_INVALID_ARG
     assert call(r=49) == nq.NQ_ERR_INVALID_ARG
+    assert call(m=1 << 20, n=1 << 19, r=4096) == nq.NQ_ERR_INVALID_ARG
     assert call(rho=0.0) == nq.NQ_ERR_INVALID_ARG
     assert call(rho=float("nan")) == nq.NQ_ERR_INVALID_ARG
     assert call(iters=-1) == nq.NQ_ERR_INVALID_ARG
