@@ -2,9 +2,10 @@
 // magnitude balancing of the scale vectors.
 //
 // Reading of the hardwired.dev NanoQuant article, section "Trikrokovy
-// pipeline", step 2 and the paragraph after it (ADMM alternating a
-// closed-form least-squares solve for the continuous part with a projection
-// onto the binary set; then power-of-two balancing of the scales).  With an
+// pipeline", step 2 and the paragraph after it (an ADMM method whose
+// iterations solve for the real-valued part by least squares in closed form
+// and map onto the +-1 set by taking signs; then balancing of the scales,
+// here by powers of two).  With an
 // identity Hessian the problem is
 //
 //     minimise ||W - A B^T||_F^2,  A = diag(pA) U diag(qA),  B = diag(pB) V diag(qB)

@@ -217,8 +217,8 @@ nq_status nq_linear_fwd_profiled(const nq_layer* L, const void* x, int32_t x_dty
 
 /* Initialiser of the factors from a dense weight (hardwired.dev NanoQuant
  * page, section "Trikrokovy pipeline", step 2 and the paragraph after it:
- * ADMM that alternates a closed-form least-squares solve of the continuous
- * part with a projection onto the binary set).  Reading, with an identity
+ * an ADMM method whose iterations solve for the real-valued part by least
+ * squares in closed form and then map onto the +-1 set by taking signs).  Reading, with an identity
  * Hessian: minimise ||W - A B^T||_F^2 with A = diag(s1) U diag(qA) and
  * B = diag(s2) V diag(qB); `iters` ADMM steps of penalty rho from the latent
  * factors A0, B0:
@@ -243,13 +243,13 @@ nq_status nq_admm_factorize(const float* W, int32_t m, int32_t n, int32_t r, con
                             float* g, float* s2, float* err, void* workspace, size_t workspace_bytes,
                             nq_stream_t stream);
 
-/* Magnitude balancing (same page and section, the paragraph after step 2:
- * the scale factors are evened out so that the binary factors have a balanced
- * range).  In place on device fp32 s1 (m), g (r), s2 (n): s1 *= c, s2 *= d,
- * g /= c d with c, d the powers of two that put the root-mean-square of s1
- * and of s2 in [1, 2) (1 for a zero or non-finite one).  W_hat is unchanged
- * bit for bit.  NQ_ERR_INVALID_ARG for null pointers or dimensions out of
- * range.  Asynchronous on `stream`. */
+/* Magnitude balancing (same page and section, the paragraph after step 2,
+ * which applies it after the initialiser to the scale factors).  In place on
+ * device fp32 s1 (m), g (r), s2 (n): s1 *= c, s2 *= d, g /= c d with c, d the
+ * powers of two that put the root-mean-square of s1 and of s2 in [1, 2) (1 for
+ * a zero or non-finite one), so neither side's scales sit far from unit size.
+ * W_hat is unchanged bit for bit.  NQ_ERR_INVALID_ARG for null pointers or
+ * dimensions out of range.  Asynchronous on `stream`. */
 nq_status nq_balance_scales(float* s1, float* g, float* s2, int32_t m, int32_t n, int32_t r, nq_stream_t stream);
 
 /* Average bits per original weight: (r(m+n) + scale_bits (m+n+r)) / (m n)

@@ -6,11 +6,10 @@ it imports nothing from the HIP package.
 
 Source: hardwired.dev NanoQuant article, section "Trikrokovy pipeline",
 step 2 (LB-ADMM) and the paragraph after it.  There the initialiser is an
-ADMM solver for the discrete choice of sign matrices and scales that best
-reproduce a weight: it alternates a closed-form least-squares solve for the
-continuous parameters with a projection onto the binary set (a sign
-operation), and is followed by magnitude balancing, which evens out the scale
-factors so that the binary factors have a balanced range.  The article gives
+ADMM method for the discrete choice of sign matrices and scales that best
+reproduce a weight: each iteration solves for the real-valued part by least
+squares in closed form and maps onto the +-1 set by taking signs; a
+magnitude-balancing step on the scale factors follows it.  The article gives
 no equation, no penalty parameter and no iteration count.  Plainest reading (identity Hessian: no
 calibration data here, so every weight counts the same):
 
