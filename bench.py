@@ -16,11 +16,17 @@ linear r(m+n)/8 sign bytes + 2(m+n+r) scale bytes + 2Bm y bytes, plus 2Bn x
 bytes per group.  `roofline` is for the dominant kernel (largest share of the
 step), timed with HIP events around each of its launches on the stream it runs
 on.  After the timed region one layer of every distinct shape of block 0 is
-checked against the fp64 oracle on the host (`parity`).
+checked against the fp64 oracle on the host (`parity`).  Further sections of
+the same line: `read_probe` (achievable read rates), `prefill` (2048-token
+GEMMs, MFMA utilisation), `initializer` (one ADMM step on a 7B shape),
+`variants` (transposed product and rank-l envelope on a 70B shape) and
+`cpu_baseline` (the fp64 oracle on the host cores).
 
   python bench.py [--steps K --warmup W]           70B decode chain (the metric)
+  python bench.py --batch B                        the same chain at batch B (B > 4 in passes of four rows)
   python bench.py --suite 7b --out FILE            7B shapes, B in {1,2,4,8,16}, 0.55/0.8/1.0 bpw:
                                                    per-shape GB/s over >= 1 GiB of rotating layer copies
+  python bench.py --initializer-only | --variants-only
 """
 from __future__ import annotations
 
