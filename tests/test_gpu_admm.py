@@ -75,7 +75,7 @@ def test_planted_recovery_matches_oracle(m, n, r):
     assert np.max(np.abs(err - rerr)) < 1e-4
 
 
-@pytest.mark.parametrize("m,n,r", [(200, 136, 24), (64, 64, 64), (300, 190, 40)])
+@pytest.mark.parametrize("m,n,r", [(200, 136, 24), (64, 64, 64), (300, 190, 40), (520, 390, 130)])
 def test_random_weight_matches_oracle(m, n, r):
     rng = np.random.default_rng(100 + m)
     W = rng.standard_normal((m, n)).astype(np.float32)
