@@ -64,12 +64,14 @@ def test_single_layer_group_equals_decode_path_bit_for_bit():
         assert np.array_equal(yg, yd)
 
 
-@pytest.mark.parametrize("B", [5, 17])
-def test_group_beyond_fused_batch_runs_in_passes(B):
+@pytest.mark.parametrize("B,shapes,n", [(5, [(300, 129), (64, 40)], 520), (17, [(300, 129), (64, 40)], 520),
+                                         (6, [(17, 257), (1, 1), (100, 130)], 129)])
+def test_group_beyond_fused_batch_runs_in_passes(B, shapes, n):
     """B > 4 runs as passes of four rows (and one of B mod 4) through the fused
     group path: every output against the oracle, and every pass equal bit for
-    bit to the group call on its rows alone."""
-    Ls, layers = _group([(300, 129), (64, 40)], 520, B, cfg=39)
+    bit to the group call on its rows alone (n = 129: later passes start at
+    rows that are not 16-byte aligned)."""
+    Ls, layers = _group(shapes, n, B, cfg=39)
     yg = _run_group(Ls, layers, torch.float32)
     for L, y in zip(Ls, yg):
         assert G.rel_l2(y, G.oracle(L, "factored")) <= 3e-4
