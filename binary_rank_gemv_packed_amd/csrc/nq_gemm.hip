@@ -1,5 +1,7 @@
 // Large-batch forward ("gemm" path, prefill): both sign-matrix products as
-// dense fp16 MFMA GEMMs with the sign bits unpacked to exact fp16 +-1 in LDS.
+// dense fp16 MFMA GEMMs.  The activation operand is staged through LDS; the
+// sign operand stays packed (one bit per weight) in LDS and each wave expands
+// its own B fragments to exact fp16 +-1 in registers.
 //
 //   prep  : X' = s2 * x per row, scaled by a per-row power of two 2^-e and
 //           rounded to fp16 (columns padded to whole 128-column tiles with 0)
@@ -22,9 +24,11 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BKG = 32;  // block tile and K step
-constexpr int LDA_S = BKG + 8;               // LDS row stride in halves (pad against bank conflicts)
+constexpr int BM = 128, BN = 128, BKG = 64;  // block tile and K step (two 32-column sign groups)
+constexpr int KG = BKG / 32;                 // sign words per W row per K step
+constexpr int LDA_S = BKG + 8;               // LDS row stride of A in halves (pad against bank conflicts)
 constexpr int TARGET_EXP = 13;               // row maximum lands in [2^13, 2^14)
 
 __device__ inline int frexp_exp(float a) { return __builtin_amdgcn_frexp_expf(a); }
@@ -87,31 +91,31 @@ struct GemmArgs {
   int MB, NB;  // block counts
 };
 
-// Unpacks one packed word (row n, columns 32g .. 32g+31 of a tile, bit 4p+j =
-// column 8j+p, bit 1 = +1) into 32 fp16 +-1 values in column order.
-__device__ __forceinline__ uint4 unpack_plane(uint32_t nw, int j) {
-  const uint32_t t = (nw >> j) & 0x11111111u;  // bit 4p = "column 8j+p is -1"
-  uint32_t d[4];
+// One plane of a sign word as the 8 fp16 +-1 values of an MFMA B fragment.
+// The word covers row n, columns 32g .. 32g+31 of a tile, bit 4p + j for
+// column 8j + p (bit set = +1), and half p of the result is column 8j + p.
+// ev = ~word & (0x01010101 << j) keeps the "-1" bits of the even halves (half
+// 2q at bit j of byte q), od = (~word & (0x10101010 << j)) >> 4 those of the
+// odd halves (half 2q + 1 at bit j of byte q).  One byte permute puts byte q
+// of each at bits 8 + j and 24 + j with nothing else set, and one shift-or by
+// sh = 7 - j moves them to the fp16 sign bits 15 and 31 and adds the
+// magnitude 1.0: two integer operations per pair of values, on the lane that
+// consumes them.
+__device__ __forceinline__ h8 sign_plane(uint32_t ev, uint32_t od, int sh) {
+  u32x4 d;
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    const uint32_t two = (t >> (8 * q)) & 0x11u;              // bits 0 and 4: columns 2q, 2q+1
-    d[q] = ((two * 0x08008000u) & 0x80008000u) | 0x3C003C00u;  // sign bits 15 and 31 on +-1.0
+    // result byte 1 = ev byte q, byte 3 = od byte q, bytes 0 and 2 = 0
+    const uint32_t sel = 0x0Cu | ((uint32_t)q << 8) | (0x0Cu << 16) | ((uint32_t)(4 + q) << 24);
+    d[q] = (__builtin_amdgcn_perm(od, ev, sel) << sh) | 0x3C003C00u;
   }
-  return uint4{d[0], d[1], d[2], d[3]};
-}
-
-__device__ __forceinline__ void unpack_word(uint32_t w, uint4& u0, uint4& u1, uint4& u2, uint4& u3) {
-  const uint32_t nw = ~w;
-  u0 = unpack_plane(nw, 0);
-  u1 = unpack_plane(nw, 1);
-  u2 = unpack_plane(nw, 2);
-  u3 = unpack_plane(nw, 3);
+  return __builtin_bit_cast(h8, d);
 }
 
 template <int EPI, typename SC>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) _Float16 As[2][BM * LDA_S];
-  __shared__ __align__(16) _Float16 Ws[2][BN * LDA_S];
+  __shared__ __align__(16) uint32_t Ws[2][BN * KG];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware tile order: the 8 XCDs take contiguous runs of tiles, M-block
@@ -126,48 +130,44 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
   const int Kpad = a.KT * 128;
   const int nk = Kpad / BKG;
 
-  // global -> register staging: A 128 rows x 32 halves (2 x 16 B per thread),
-  // W 8 row tiles x 16 words (threads 0..127, one word each)
-  const int a_row = tid >> 1, a_col = (tid & 1) * 16;
-  const int a_grow = min(m0 + a_row, a.M - 1);
-  const _Float16* a_src = a.A + (size_t)a_grow * Kpad + a_col;
-  const int w_rt = tid >> 4, w_l = tid & 15;               // row tile in block, row in tile
-  const int w_row = n0 + w_rt * 16 + w_l;
-  const bool w_active = tid < 128;
-  const int w_rtg = min((n0 >> 4) + w_rt, (a.N + 15) / 16 - 1);
+  // global -> register staging.  A: 128 rows x 64 halves as 1024 16-byte
+  // chunks; chunk 256 i + tid is row 32 i + tid / 8, columns 8 (tid % 8) .. +7,
+  // so one load instruction covers 8 whole 128-byte row segments (rows past M
+  // re-read row M - 1; their results are never stored).  W: the packed word of
+  // block row tid / 2, sign group tid % 2 of the step (row tiles past the last
+  // re-read it).  The signs stay packed in LDS; each wave expands its own B
+  // fragments in registers.
+  const int a_row = tid >> 3, a_col = (tid & 7) * 8;
+  const _Float16* a_src0 = a.A + (size_t)min(m0 + a_row, a.M - 1) * Kpad + a_col;
+  const _Float16* a_src1 = a.A + (size_t)min(m0 + a_row + 32, a.M - 1) * Kpad + a_col;
+  const _Float16* a_src2 = a.A + (size_t)min(m0 + a_row + 64, a.M - 1) * Kpad + a_col;
+  const _Float16* a_src3 = a.A + (size_t)min(m0 + a_row + 96, a.M - 1) * Kpad + a_col;
+  const int w_row = tid >> 1, w_g = tid & 1, w_l = w_row & 15;
+  const int w_rtg = min((n0 >> 4) + (w_row >> 4), (a.N + 15) / 16 - 1);
   const uint32_t* w_tile = a.W + (size_t)w_rtg * a.KT * 64;
 
-  uint4 ra0, ra1;
-  uint32_t rw = 0;
+  uint4 ra0, ra1, ra2, ra3;
+  uint32_t rw;
 #define NQ_GLOAD(ks)                                                          \
   do {                                                                        \
     const int k0_ = (ks) * BKG;                                               \
-    const uint4* s_ = reinterpret_cast<const uint4*>(a_src + k0_);            \
-    ra0 = s_[0];                                                              \
-    ra1 = s_[1];                                                              \
-    if (w_active) {                                                           \
-      const int kt_ = k0_ >> 7, g_ = (k0_ >> 5) & 3;                          \
-      const int q_ = kt_ >> 2;                                                \
-      const int f_ = min(4, a.KT - 4 * q_);                                   \
-      rw = w_tile[(size_t)q_ * 256 + (w_l + 16 * g_) * f_ + (kt_ & 3)];       \
-    }                                                                         \
+    ra0 = *reinterpret_cast<const uint4*>(a_src0 + k0_);                      \
+    ra1 = *reinterpret_cast<const uint4*>(a_src1 + k0_);                      \
+    ra2 = *reinterpret_cast<const uint4*>(a_src2 + k0_);                      \
+    ra3 = *reinterpret_cast<const uint4*>(a_src3 + k0_);                      \
+    const int kt_ = k0_ >> 7, g_ = ((k0_ >> 5) & 3) + w_g;                    \
+    const int q_ = kt_ >> 2;                                                  \
+    const int f_ = min(4, a.KT - 4 * q_);                                     \
+    rw = w_tile[(size_t)q_ * 256 + (w_l + 16 * g_) * f_ + (kt_ & 3)];         \
   } while (0)
-#define NQ_LSTORE(buf)                                                                    \
-  do {                                                                                    \
-    uint4* da_ = reinterpret_cast<uint4*>(&As[(buf)][a_row * LDA_S + a_col]);             \
-    da_[0] = ra0;                                                                         \
-    da_[1] = ra1;                                                                         \
-    if (w_active) {                                                                       \
-      uint4 u0_, u1_, u2_, u3_;                                                           \
-      unpack_word(rw, u0_, u1_, u2_, u3_);                                                \
-      uint4* dw_ = reinterpret_cast<uint4*>(&Ws[(buf)][(w_rt * 16 + w_l) * LDA_S]);       \
-      dw_[0] = u0_;                                                                       \
-      dw_[1] = u1_;                                                                       \
-      dw_[2] = u2_;                                                                       \
-      dw_[3] = u3_;                                                                       \
-    }                                                                                     \
+#define NQ_LSTORE(buf)                                                                     \
+  do {                                                                                     \
+    *reinterpret_cast<uint4*>(&As[(buf)][(a_row + 0) * LDA_S + a_col]) = ra0;              \
+    *reinterpret_cast<uint4*>(&As[(buf)][(a_row + 32) * LDA_S + a_col]) = ra1;             \
+    *reinterpret_cast<uint4*>(&As[(buf)][(a_row + 64) * LDA_S + a_col]) = ra2;             \
+    *reinterpret_cast<uint4*>(&As[(buf)][(a_row + 96) * LDA_S + a_col]) = ra3;             \
+    Ws[(buf)][w_row * KG + w_g] = rw;                                                      \
   } while (0)
-  (void)w_row;
 
   // wave tile 64 x 64 = 4 x 4 MFMA tiles of 16 x 16
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -181,18 +181,30 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
   NQ_LSTORE(0);
   __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;  // fragment row/column and K offset
+  const int sh = 7 - (lane >> 4);                  // plane j = lane / 16 of each sign word
+  const uint32_t emask = 0x01010101u << (lane >> 4), omask = emask << 4;
   for (int ks = 0; ks < nk; ks++) {
     const int buf = ks & 1;
     if (ks + 1 < nk) NQ_GLOAD(ks + 1);
-    h8 af[4], bf[4];
+    uint2 wv[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) af[i] = *reinterpret_cast<const h8*>(&As[buf][(wm + 16 * i + fr) * LDA_S + fk]);
+    for (int j = 0; j < 4; j++) wv[j] = *reinterpret_cast<const uint2*>(&Ws[buf][(wn + 16 * j + fr) * KG]);
 #pragma unroll
-    for (int j = 0; j < 4; j++) bf[j] = *reinterpret_cast<const h8*>(&Ws[buf][(wn + 16 * j + fr) * LDA_S + fk]);
+    for (int s = 0; s < KG; s++) {
+      h8 af[4], bf[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 4; i++)
+        af[i] = *reinterpret_cast<const h8*>(&As[buf][(wm + 16 * i + fr) * LDA_S + 32 * s + fk]);
 #pragma unroll
-      for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; j++) {
+        const uint32_t nw = ~(s == 0 ? wv[j].x : wv[j].y);
+        bf[j] = sign_plane(nw & emask, (nw & omask) >> 4, sh);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
     if (ks + 1 < nk) NQ_LSTORE(buf ^ 1);
     __syncthreads();
   }
