@@ -450,6 +450,7 @@ def run_prefill70b(dev, tokens=2048, bpw=0.8, reps=5):
                                                                            MFMA_PEAK_FP16_TFLOPS, 4),
                      "gemm_tu_ms": round(per[3], 4), "gemm_tu_util": round(f2 / (per[3] * 1e-3) / 1e12 /
                                                                            MFMA_PEAK_FP16_TFLOPS, 4),
+                     "prep_ms": round(per[0], 4), "mid_ms": round(per[2], 4),
                      "sampled_rows_rel_l2": float(f"{e:.3e}"), "bf16_rounding_rel_l2": float(f"{er:.3e}"),
                      "ok": bool(e <= 2e-3 + er)}
         c = {"q": 2, "k": 2, "gate": 2, "down": 1}[name]  # q~o, k~v, gate~up

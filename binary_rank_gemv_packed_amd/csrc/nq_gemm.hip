@@ -57,28 +57,95 @@ __device__ inline int row_exp(float mx) {
   return (frexp_exp(mx) - 1) - TARGET_EXP;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// V consecutive values p[k .. k+V-1] as fp32 (V = 4: one vector load; the
+// caller guarantees the alignment)
+template <int V, typename T> __device__ inline f32x4 ldv(const T* p, size_t k);
+template <> __device__ inline f32x4 ldv<1, float>(const float* p, size_t k) { return f32x4{p[k], 0.f, 0.f, 0.f}; }
+template <> __device__ inline f32x4 ldv<1, _Float16>(const _Float16* p, size_t k) {
+  return f32x4{(float)p[k], 0.f, 0.f, 0.f};
+}
+template <> __device__ inline f32x4 ldv<1, uint16_t>(const uint16_t* p, size_t k) {
+  return f32x4{ldf(p, k), 0.f, 0.f, 0.f};
+}
+template <> __device__ inline f32x4 ldv<4, float>(const float* p, size_t k) {
+  return *reinterpret_cast<const f32x4*>(p + k);
+}
+template <> __device__ inline f32x4 ldv<4, _Float16>(const _Float16* p, size_t k) {
+  return __builtin_convertvector(*reinterpret_cast<const f16x4*>(p + k), f32x4);
+}
+template <> __device__ inline f32x4 ldv<4, uint16_t>(const uint16_t* p, size_t k) {
+  const u16x4 b = *reinterpret_cast<const u16x4*>(p + k);
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; i++) r[i] = __uint_as_float((uint32_t)b[i] << 16);
+  return r;
+}
+
 // One workgroup (256 threads) per row: out[row][k] = fp16(scale_in[k] * in[row][k] * 2^-e)
-// for k < K, 0 for K <= k < Kpad; rexp[row] = e.
-template <typename IT, typename ST>
-__global__ void __launch_bounds__(256) row_to_f16_kernel(const IT* __restrict__ in, size_t ld_in,
-                                                         const ST* __restrict__ scale, int K, int Kpad,
-                                                         _Float16* __restrict__ out, int* __restrict__ rexp) {
+// for k < K, 0 for K <= k < Kpad; rexp[row] = e.  in[row][k] is the sum of
+// nsplit partial copies split_stride elements apart (the K splits of the GEMM
+// that wrote them), added in copy order.  Each thread takes V consecutive
+// columns at a time (V = 4 needs K, ld_in and split_stride multiples of 4 and
+// in, scale aligned to 4 elements).
+template <typename IT, typename ST, int V>
+__global__ void __launch_bounds__(256) row_to_f16_kernel(const IT* __restrict__ in, size_t ld_in, int nsplit,
+                                                         size_t split_stride, const ST* __restrict__ scale, int K,
+                                                         int Kpad, _Float16* __restrict__ out,
+                                                         int* __restrict__ rexp) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const IT* src = in + (size_t)row * ld_in;
+  auto value = [&](int k) {
+    f32x4 v = ldv<V>(src, k);
+    for (int s = 1; s < nsplit; s++) v += ldv<V>(src + s * split_stride, k);
+    return v * ldv<V>(scale, k);
+  };
   float mx = 0.0f;
-  for (int k = threadIdx.x; k < K; k += 256) mx = fmaxf(mx, fabsf(ldf(src, k) * ldf(scale, k)));
+  for (int k = V * threadIdx.x; k < K; k += 256 * V) {
+    const f32x4 v = value(k);
+#pragma unroll
+    for (int i = 0; i < V; i++) mx = fmaxf(mx, fabsf(v[i]));
+  }
   mx = block_max(mx, red);
   const int e = row_exp(mx);
   const float f = __builtin_ldexpf(1.0f, -e);
   _Float16* dst = out + (size_t)row * Kpad;
-  for (int k = threadIdx.x; k < Kpad; k += 256) dst[k] = k < K ? (_Float16)(ldf(src, k) * ldf(scale, k) * f) : (_Float16)0.0f;
+  for (int k = V * threadIdx.x; k < Kpad; k += 256 * V) {
+    const f32x4 v = k < K ? value(k) * f : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (V == 4) {
+      *reinterpret_cast<f16x4*>(dst + k) = __builtin_convertvector(v, f16x4);
+    } else {
+      dst[k] = (_Float16)v[0];
+    }
+  }
   if (threadIdx.x == 0) rexp[row] = e;
+}
+
+// Launches row_to_f16_kernel with V = 4 where the sizes and pointers allow it.
+template <typename IT, typename ST>
+void launch_row_to_f16(hipStream_t st, int rows, const IT* in, size_t ld_in, int nsplit, size_t split_stride,
+                       const ST* scale, int K, int Kpad, _Float16* out, int* rexp) {
+  const bool v4 = K % 4 == 0 && ld_in % 4 == 0 && split_stride % 4 == 0 &&
+                  reinterpret_cast<uintptr_t>(in) % (4 * sizeof(IT)) == 0 &&
+                  reinterpret_cast<uintptr_t>(scale) % (4 * sizeof(ST)) == 0;
+  if (v4)
+    hipLaunchKernelGGL((row_to_f16_kernel<IT, ST, 4>), dim3(rows), dim3(256), 0, st, in, ld_in, nsplit, split_stride,
+                       scale, K, Kpad, out, rexp);
+  else
+    hipLaunchKernelGGL((row_to_f16_kernel<IT, ST, 1>), dim3(rows), dim3(256), 0, st, in, ld_in, nsplit, split_stride,
+                       scale, K, Kpad, out, rexp);
 }
 
 // C = 2^e_row * (A W^T): A [M x Kpad] fp16 row-major (lda = Kpad), W the packed
 // sign matrix with N rows and KT column tiles (Kpad = 128 KT).  EPI 0: fp32 out
-// (ldc); EPI 1: out = colscale[n] * C as fp32 (ydt 0) or bf16 (ydt 2).
+// (ldc); EPI 1: out = colscale[n] * C as fp32 (ydt 0) or bf16 (ydt 2).  With
+// S > 1 (EPI 0 only) the K steps are cut into S contiguous ranges, one
+// workgroup per (tile, range), and range s writes its partial C at
+// C + s * split_stride; the consumer adds the S partials.
 struct GemmArgs {
   const _Float16* A;
   const int* rexp;
@@ -89,6 +156,8 @@ struct GemmArgs {
   const void* colscale;
   int ydt;
   int MB, NB;  // block counts
+  int S;       // K splits
+  size_t split_stride;
 };
 
 // One plane of a sign word as the 8 fp16 +-1 values of an MFMA B fragment.
@@ -120,15 +189,18 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware tile order: the 8 XCDs take contiguous runs of tiles, M-block
   // major, so the workgroups one XCD runs together share an activation block
-  const int T = a.MB * a.NB;
-  const int per = (T + 7) / 8;
+  const int T = a.MB * a.NB, TS = T * a.S;
+  const int per = (TS + 7) / 8;
   const int id = blockIdx.x;
-  const int t = (id % 8) * per + id / 8;
-  if (t >= T) return;
+  const int ts = (id % 8) * per + id / 8;
+  if (ts >= TS) return;
+  const int t = ts % T, split = ts / T;
   const int mb = t / a.NB, nb = t % a.NB;
   const int m0 = mb * BM, n0 = nb * BN;
   const int Kpad = a.KT * 128;
-  const int nk = Kpad / BKG;
+  const int nk_all = Kpad / BKG, nks = (nk_all + a.S - 1) / a.S;
+  const int kbeg = split * nks;
+  const int nk = min(nk_all - kbeg, nks);  // K steps of this range (<= 0: an empty range, writes zeros)
 
   // global -> register staging.  A: 128 rows x 64 halves as 1024 16-byte
   // chunks; chunk 256 i + tid is row 32 i + tid / 8, columns 8 (tid % 8) .. +7,
@@ -177,15 +249,17 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  NQ_GLOAD(0);
-  NQ_LSTORE(0);
+  if (nk > 0) {
+    NQ_GLOAD(kbeg);
+    NQ_LSTORE(0);
+  }
   __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;  // fragment row/column and K offset
   const int sh = 7 - (lane >> 4);                  // plane j = lane / 16 of each sign word
   const uint32_t emask = 0x01010101u << (lane >> 4), omask = emask << 4;
   for (int ks = 0; ks < nk; ks++) {
     const int buf = ks & 1;
-    if (ks + 1 < nk) NQ_GLOAD(ks + 1);
+    if (ks + 1 < nk) NQ_GLOAD(kbeg + ks + 1);
     uint2 wv[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) wv[j] = *reinterpret_cast<const uint2*>(&Ws[buf][(wn + 16 * j + fr) * KG]);
@@ -225,7 +299,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
         if (col >= a.N) continue;
         const float c = acc[i][j][v] * rs;
         if (EPI == 0) {
-          reinterpret_cast<float*>(a.C)[(size_t)row * a.ldc + col] = c;
+          reinterpret_cast<float*>(a.C)[split * a.split_stride + (size_t)row * a.ldc + col] = c;
         } else {
           const float yv = c * ldf(reinterpret_cast<const SC*>(a.colscale), col);
           const size_t yi = (size_t)row * a.ldc + col;
@@ -246,6 +320,14 @@ GemmPlan gemm_plan(int m, int n, int r, int B) {
   p.KT2 = ceil_div(r, 128);  // stage 2 contraction: rank
   p.RT1 = ceil_div(r, 16);
   p.RT2 = ceil_div(m, 16);
+  // K splits of the first GEMM when its tiles alone cannot fill the 256 CUs
+  // (a small rank: k and v of a 70B block have 96 tiles at 2048 tokens):
+  // double S while there are fewer than 384 (tile, range) pairs, each range
+  // keeps at least 4 K steps, and S <= 8; then drop splits that would be empty.
+  const int T1 = ceil_div(B, BM) * ceil_div(r, BN), nk1 = p.KT1 * 128 / BKG;
+  int S = 1;
+  while (T1 * S < 384 && S < 8 && nk1 / (2 * S) >= 4) S *= 2;
+  p.S1 = ceil_div(nk1, ceil_div(nk1, S));
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -254,7 +336,7 @@ GemmPlan gemm_plan(int m, int n, int r, int B) {
   };
   p.off_x16 = take((size_t)B * p.KT1 * 128 * 2);  // X' fp16
   p.off_xexp = take((size_t)B * 4);
-  p.off_t32 = take((size_t)B * r * 4);            // T fp32
+  p.off_t32 = take((size_t)p.S1 * B * r * 4);     // T fp32, one partial per K split
   p.off_t16 = take((size_t)B * p.KT2 * 128 * 2);  // T' fp16
   p.off_texp = take((size_t)B * 4);
   p.bytes = o;
@@ -278,16 +360,19 @@ static hipError_t gemm_forward_t(const FwdArgs& a, const GemmPlan& p) {
   const int B = a.B;
 
   mark(a, dim3(B), dim3(256));
-  hipLaunchKernelGGL((row_to_f16_kernel<XT, ST>), dim3(B), dim3(256), 0, st, reinterpret_cast<const XT*>(a.x),
-                     (size_t)a.n, s2, a.n, p.KT1 * 128, x16, xexp);
-  GemmArgs g1{x16, xexp, Vt, B, a.r, p.KT1, t32, (size_t)a.r, nullptr, 0, ceil_div(B, BM), ceil_div(a.r, BN)};
-  mark(a, dim3(8 * ceil_div(g1.MB * g1.NB, 8)), dim3(256));
-  hipLaunchKernelGGL((gemm_kernel<0, ST>), dim3(8 * ceil_div(g1.MB * g1.NB, 8)), dim3(256), 0, st, g1);
+  launch_row_to_f16(st, B, reinterpret_cast<const XT*>(a.x), (size_t)a.n, 1, (size_t)0, s2, a.n, p.KT1 * 128, x16,
+                    xexp);
+  const size_t tstride = (size_t)B * a.r;  // elements between the K-split partials of T
+  GemmArgs g1{x16, xexp, Vt, B, a.r, p.KT1, t32, (size_t)a.r, nullptr, 0, ceil_div(B, BM), ceil_div(a.r, BN),
+              p.S1, tstride};
+  const dim3 grid1(8 * ceil_div(g1.MB * g1.NB * g1.S, 8));
+  mark(a, grid1, dim3(256));
+  hipLaunchKernelGGL((gemm_kernel<0, ST>), grid1, dim3(256), 0, st, g1);
   mark(a, dim3(B), dim3(256));
-  hipLaunchKernelGGL((row_to_f16_kernel<float, ST>), dim3(B), dim3(256), 0, st, t32, (size_t)a.r, g, a.r,
-                     p.KT2 * 128, t16, texp);
+  launch_row_to_f16(st, B, static_cast<const float*>(t32), (size_t)a.r, p.S1, tstride, g, a.r, p.KT2 * 128, t16,
+                    texp);
   GemmArgs g2{t16, texp, U, B, a.m, p.KT2, a.y, (size_t)a.m, s1, a.y_dtype == 0 ? 0 : 2, ceil_div(B, BM),
-              ceil_div(a.m, BN)};
+              ceil_div(a.m, BN), 1, 0};
   mark(a, dim3(8 * ceil_div(g2.MB * g2.NB, 8)), dim3(256));
   hipLaunchKernelGGL((gemm_kernel<1, ST>), dim3(8 * ceil_div(g2.MB * g2.NB, 8)), dim3(256), 0, st, g2);
   mark(a);

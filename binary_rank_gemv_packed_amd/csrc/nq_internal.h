@@ -136,6 +136,7 @@ hipError_t valu_forward(const FwdArgs& a, const ValuPlan& p);
 
 struct GemmPlan {
   int Bpad, KT1, KT2, RT1, RT2;
+  int S1;  // K splits of the first GEMM (partials summed by the mid kernel)
   size_t off_x16, off_xexp, off_t32, off_t16, off_texp;
   size_t bytes;
 };

@@ -52,6 +52,40 @@ def test_prefill_exact_integers():
     assert np.array_equal(y, ref)
 
 
+def test_prefill_ksplit_exact_integers():
+    """A small-rank shape (6 output tiles, 34 K steps) whose first GEMM runs in
+    7 K ranges (5 steps each, the last 4), the partials summed by the mid
+    kernel.  x is zero except 48 columns spread over all ranges, so every
+    partial and every fp16 operand is a small integer or half-integer and the
+    fp32 result is exact."""
+    m, n, r, B = 200, 2100, 150, 300
+    L = synth.make_integer_layer(m, n, r, B, seed=11)
+    keep = np.linspace(0, n - 1, 48).astype(int)
+    mask = np.zeros(n, bool)
+    mask[keep] = True
+    L.x[:, ~mask] = 0.0
+    layer = G.pack_layer(L)
+    # the workspace beyond the two fp16 operand copies holds the fp32 T: more
+    # than one B x r partial of it means the K split is taken
+    f16_copies = B * (-(-n // 128) * 128 + -(-r // 128) * 128) * 2
+    assert nq.workspace_bytes(layer, B, "gemm") - f16_copies >= 2 * B * r * 4
+    ref = G.oracle(L, "factored")
+    y = G.run(L, layer, y_dtype=torch.float32)
+    assert np.array_equal(y, ref)
+
+
+def test_prefill_ksplit_parity():
+    """The same split shape with random fp16 scales and inputs, fp32 and bf16
+    outputs, against the fp64 oracle."""
+    L = synth.make_layer(200, 2100, 150, 300, cfg=5, layer=4)
+    layer = G.pack_layer(L)
+    ref = G.oracle(L, "dense")
+    y32 = G.run(L, layer, y_dtype=torch.float32)
+    ybf = G.run(L, layer, y_dtype=torch.bfloat16)
+    assert G.rel_l2(y32, ref) <= TOL32
+    G.check_bf16_output(ybf, ref, y32)
+
+
 def test_prefill_batch_rows_independent():
     L = synth.make_layer(500, 400, 200, 64, cfg=6)
     layer = G.pack_layer(L)
