@@ -67,6 +67,7 @@ def parse():
     ap.add_argument("--no-variants", action="store_true", help="skip the transposed / envelope section")
     ap.add_argument("--variants-only", action="store_true", help="run only the transposed / envelope section")
     ap.add_argument("--initializer-only", action="store_true", help="run only the ADMM initialiser section")
+    ap.add_argument("--prefill-only", action="store_true", help="run only the 2048-token prefill section")
     ap.add_argument("--suite", default=None, choices=["7b"])
     ap.add_argument("--out", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -950,6 +951,8 @@ def main():
         print(json.dumps({"initializer": run_initializer("cuda:0")}), flush=True)
     elif args.variants_only:
         print(json.dumps({"variants": run_variants("cuda:0")}), flush=True)
+    elif args.prefill_only:
+        print(json.dumps({"prefill": run_prefill70b("cuda:0")}), flush=True)
     else:
         run_decode70b(args)
 
