@@ -54,8 +54,9 @@ typedef enum {
   NQ_PATH_AUTO = 0,
   NQ_PATH_GEMV = 1,   /* 1 <= B <= 16: sign bits as fp4 MFMA operands, activations as fp8
                          pieces read from global images (4 or 5 launches)                    */
-  NQ_PATH_GEMM = 2,   /* any B (auto for B > 16, prefill): +-1 signs unpacked to fp16 in LDS,
-                         fp16 MFMA with per-row power-of-two activation scales, fp32 accumulate */
+  NQ_PATH_GEMM = 2,   /* any B (auto for B > 16, prefill): signs packed in LDS, expanded to
+                         fp16 +-1 in registers; fp16 MFMA with per-row power-of-two activation
+                         scales, fp32 accumulate                                             */
   NQ_PATH_VALU = 3,   /* B == 1 only: plain per-bit masked sums on the vector ALU (comparison) */
   NQ_PATH_DECODE = 4  /* 1 <= B <= 16: the decode path, activation images staged in LDS
                          (2 launches per chunk of <= 4 batch rows, 3 when the stage-1
