@@ -86,6 +86,21 @@ def test_prefill_ksplit_parity():
     G.check_bf16_output(ybf, ref, y32)
 
 
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale_dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n,r", [(1024, 200), (1030, 201)])
+def test_prefill_dtypes(x_dtype, scale_dtype, n, r):
+    """Every activation / scale dtype pair on the prefill path, with column
+    counts that are (n = 1024, r = 200) and are not (1030, 201) multiples of
+    four, so the row kernels run both their four-column and one-column forms;
+    both shapes also take the K split (2 output tiles; 16 and 18 K steps in 4
+    ranges, the last of the second one shorter)."""
+    L = synth.make_layer(150, n, r, 40, cfg=5, layer=n + r, x_dtype=x_dtype, scale_dtype=scale_dtype)
+    ref = G.oracle(L, "dense")
+    y = G.run(L, y_dtype=torch.float32)
+    assert G.rel_l2(y, ref) <= TOL32
+
+
 def test_prefill_batch_rows_independent():
     L = synth.make_layer(500, 400, 200, 64, cfg=6)
     layer = G.pack_layer(L)
